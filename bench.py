@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-key scoring hot path on one MI355X.
+
+One step = the whole path over one batch: tq_query_transform (A = Pi q,
+T = S_mat q) then tq_score (raw scores of every query against every compressed
+key). The default workload is the decode shape: B=32 queries, S=32768 keys,
+D=128, 2-bit indices + 1-bit QJL signs (3 bits per coordinate), unpacked bytes.
+
+Inputs are synthetic and already resident in HBM when timing starts. A ring of
+distinct buffer sets totalling at least 512 MB is cycled so that no step finds
+its keys in the 256 MiB Infinity Cache. The K timed steps are replayed from
+captured HIP graphs (host launch overhead would otherwise dominate microsecond
+kernels): per chunk of the ring, one graph of its query transforms and one of
+its scores. HIP events between those graph launches give each kernel's average
+duration inside the timed region. The CPU oracle is timed on a bounded sample
+as a reported baseline.
+
+Prints ONE JSON line. ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query-key scores/sec + achieved HBM GB/s, B=32 S=32768 D=128 3-bit keys"
+HBM_PEAK_GBS = 8000.0
+RING_BYTES = 512 * 1024 * 1024
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode",
+                    help="decode (default, the quoted configuration); others for profiling")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (profiling runs)")
+    ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle baseline sample")
+    return ap.parse_args()
+
+
+def build_ring(w, device, seed_base):
+    """Distinct input/output buffer sets, each a full batch of workload w."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+
+    per_set = w.key_bytes() + w.score_bytes() + 4 * w.P * w.B * w.D * 3
+    nsets = max(2, math.ceil(RING_BYTES / per_set))
+    if w.name not in ("decode", "tiny", "packed"):
+        nsets = max(2, min(nsets, 8))
+    Pi, S_mat = synth.head_matrices(w.seed, w.H, w.D)
+    cb = synth.timing_codebook(w.seed, w.C, w.D)
+    q = synth.queries(w.seed, w.P, w.B, w.D)
+    idx, sign, gamma = synth.timing_code_streams(w.seed, w.P, w.S, w.D, w.C, w.layout, w.bits)
+    base = {
+        "q": torch.from_numpy(q).to(device),
+        "idx": torch.from_numpy(idx).to(device),
+        "sign": torch.from_numpy(sign).to(device),
+        "gamma": torch.from_numpy(gamma).to(device),
+    }
+    shared = {
+        "Pi": torch.from_numpy(Pi).to(device),
+        "S_mat": torch.from_numpy(S_mat).to(device),
+        "codebook": torch.from_numpy(cb).to(device),
+    }
+    ring = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in base.items()}
+        s["A"] = torch.empty((w.P, w.B, w.D), dtype=torch.float32, device=device)
+        s["T"] = torch.empty_like(s["A"])
+        s["scores"] = torch.empty((w.P, w.B, w.S), dtype=torch.float32, device=device)
+        s["keys"] = tq.Keys(w.layout, s["idx"], s["sign"], s["gamma"], w.bits if w.layout == "packed" else 0)
+        ring.append(s)
+    torch.cuda.synchronize()
+    host = {"q": q, "Pi": Pi, "S_mat": S_mat, "codebook": cb, "idx": idx, "sign": sign, "gamma": gamma}
+    return ring, shared, host, per_set
+
+
+def make_step(w, shared, kernel):
+    import compressed_attention_scoring_amd as tq
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        tq.tq_query_transform(s["q"], shared["Pi"], shared["S_mat"], s["A"], s["T"])
+        if ev is not None:
+            ev[1].record()
+        tq.tq_score_with_kernel(s["A"], s["T"], s["keys"], shared["codebook"], kernel, s["scores"])
+        if ev is not None:
+            ev[2].record()
+    return step
+
+
+def time_phased_graphs(w, ring, shared, kernel, steps):
+    """Run exactly `steps` steps from captured HIP graphs and time each kernel.
+
+    The ring is cut into chunks of consecutive buffer sets. For a chunk, one graph
+    holds the query transforms of its sets and a second graph their scores, so
+    each batch still gets its transform and then its score. HIP events recorded
+    on the kernels' stream between the graph launches bracket runs of
+    back-to-back kernels of one kind, giving each kernel's average duration
+    without per-launch event overhead. Returns (seconds between synchronisations,
+    mean transform us, mean score us)."""
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+
+    G = len(ring)
+    chunks = [G] * (steps // G) + ([steps % G] if steps % G else [])
+    graphs = {}
+    for n in sorted(set(chunks)):
+        gq, gs = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gq):
+            for i in range(n):
+                tq.tq_query_transform(ring[i]["q"], shared["Pi"], shared["S_mat"], ring[i]["A"], ring[i]["T"])
+        with torch.cuda.graph(gs):
+            for i in range(n):
+                s = ring[i]
+                tq.tq_score_with_kernel(s["A"], s["T"], s["keys"], shared["codebook"], kernel, s["scores"])
+        graphs[n] = (gq, gs)
+    for gq, gs in graphs.values():      # one untimed replay of each graph
+        gq.replay()
+        gs.replay()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in chunks]
+    t0 = time.perf_counter()
+    for n, ev in zip(chunks, evs):
+        gq, gs = graphs[n]
+        ev[0].record()
+        gq.replay()
+        ev[1].record()
+        gs.replay()
+        ev[2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    qt_ms = sum(a.elapsed_time(b) for a, b, _ in evs)
+    sc_ms = sum(b.elapsed_time(c) for _, b, c in evs)
+    return elapsed, 1e3 * qt_ms / steps, 1e3 * sc_ms / steps
+
+
+def cpu_baseline(w, host, target_s):
+    """The float64 oracle (explicit key reconstruction) on the host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import score as osc
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    P = 1
+    S = w.S
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        for p in range(P):
+            osc.scores_by_reconstruction(host["q"][p], host["idx"][p], host["sign"][p],
+                                         host["gamma"][p].astype(np.float64), host["Pi"][p % w.H],
+                                         host["S_mat"][p % w.H], host["codebook"])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= target_s and len(times) >= 3:
+            break
+        if len(times) >= 5000:
+            break
+    med = sorted(times)[len(times) // 2]
+    pairs = P * w.B * S
+    return {
+        "value": pairs / med,
+        "unit": "scores/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{'problem 0 of ' + str(w.P) if w.P > 1 else 'the full batch'} "
+                   f"(B={w.B}, S={S}, D={w.D}) scored by float64 explicit reconstruction, "
+                   f"median of {len(times)} runs ({sum(times):.1f} s total); host {platform.processor() or platform.machine()}"),
+    }
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path shards with no "
+                                   "exchange (see the design notes) but no multi-GPU run is built",
+                          "n_gpus": args.gpus}), flush=True)
+        return 2
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    device = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.B, w.D, args.kernel)
+    log(f"workload {w.describe()} kernel {kname}")
+    ring, shared, host, per_set = build_ring(w, device, w.seed)
+    log(f"ring of {len(ring)} buffer sets, {len(ring) * per_set / 1e6:.0f} MB")
+    step = make_step(w, shared, args.kernel)
+
+    for i in range(args.warmup):
+        step(ring[i % len(ring)])
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    mode = "eager" if args.eager else "hipgraph"
+    if mode == "hipgraph":
+        elapsed, qt_us, score_us = time_phased_graphs(w, ring, shared, args.kernel, args.steps)
+    else:
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ring[i % len(ring)], evs[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        qt_us = 1e3 * sum(a.elapsed_time(b) for a, b, _ in evs) / args.steps
+        score_us = 1e3 * sum(b.elapsed_time(c) for _, b, c in evs) / args.steps
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms ({mode}); "
+        f"transform {qt_us:.2f} us, score {score_us:.2f} us per launch")
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    pairs = w.pairs
+    alg_bytes = w.algorithmic_bytes()
+    achieved = alg_bytes / (score_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": pairs / (ms_per_step * 1e-3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate",
+        "data": "synthetic: seeded random codes, N(0,1) queries, Haar rotation, Gaussian projection",
+        "config": {"workload": w.name, "P": w.P, "B": w.B, "S": w.S, "D": w.D, "C": w.C,
+                   "layout": w.layout, "bits": w.bits},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": kname,
+            "bytes_per_launch": alg_bytes,
+            "avg_launch_us": score_us,
+        },
+        "achieved_hbm_gbs": achieved,
+        "tq_score_us": score_us,
+        "tq_query_transform_us": qt_us,
+        "timing": mode,
+        "kernel_timing": ("HIP events on the kernels' stream in the timed region, around graph "
+                          "launches of back-to-back transforms and back-to-back scores"),
+        "ring_sets": len(ring),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,249 @@
+"""Compressed-key attention scoring on MI355X (gfx950): Python binding.
+
+Thin ctypes layer over the C ABI in ``include/tq.h`` (library ``libtq.so``,
+built in-tree by ``python -m compressed_attention_scoring_amd.build``). The
+functions keep the C names:
+
+    tq_query_transform(q, Pi, S_mat)           -> (A, T)
+    tq_score(A, T, keys, codebook)             -> scores
+    tq_score_with_kernel(A, T, keys, codebook, kernel)
+    tq_decode_debug(keys, D)                   -> (idx, sign, gamma)
+    tq_score_kernel_name(layout, bits, C, B, D, kernel)
+
+Only argument marshalling happens here: shapes, dtypes, contiguity and device
+are checked, output tensors are allocated with torch, and pointers plus the
+current HIP stream are handed to the library. Every step of the computation
+runs in the library's HIP kernels. There is no CPU fallback: importing this
+package raises if ``libtq.so`` is missing, and tensors not on a GPU are refused.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "Keys", "TqError", "tq_query_transform", "tq_score", "tq_score_with_kernel",
+    "tq_decode_debug", "tq_score_kernel_name", "tq_status_string", "library_path",
+    "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libtq.so")
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "tq.h")
+
+TQ_OK = 0
+TQ_UNPACKED = 0
+TQ_PACKED = 1
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+class _CKeys(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("idx", ctypes.c_void_p),
+        ("sign", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m compressed_attention_scoring_amd.build` "
+            "(needs hipcc) before using the library")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.tq_query_transform.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.tq_query_transform.restype = i32
+    lib.tq_score.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, vp, i32, i32, i32, i32, vp]
+    lib.tq_score.restype = i32
+    lib.tq_score_with_kernel.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, vp,
+                                         i32, i32, i32, i32, i32, vp]
+    lib.tq_score_with_kernel.restype = i32
+    lib.tq_score_kernel_name.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.tq_score_kernel_name.restype = ctypes.c_char_p
+    lib.tq_decode_debug.argtypes = [ctypes.POINTER(_CKeys), vp, vp, vp, i32, i32, i32, vp]
+    lib.tq_decode_debug.restype = i32
+    lib.tq_status_string.argtypes = [i32]
+    lib.tq_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def header_functions() -> list[str]:
+    """Names of the functions ``include/tq.h`` declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
+
+
+class TqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {tq_status_string(status)} (status {status})")
+
+
+def tq_status_string(status: int) -> str:
+    return _lib.tq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TqError(status, where)
+
+
+def _gpu(t: torch.Tensor, name: str, dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Keys:
+    """Compressed keys of P problems with S keys of D coordinates each.
+
+    layout "unpacked": idx uint8 [P,S,D], sign int8 [P,S,D] (+-1), gamma float32 [P,S].
+    layout "packed":   idx uint8 [P,S,D*bits/8] (LSB-first bitstream), sign uint8 [P,S,D/8]
+                       (bit 1 = +1), gamma float16 [P,S]; bits 2 or 3.
+    A leading problem axis may be omitted (P = 1).
+    """
+    layout: str
+    idx: torch.Tensor
+    sign: torch.Tensor
+    gamma: torch.Tensor
+    bits: int = 0
+
+    def _c(self, D: int):
+        if self.layout == "unpacked":
+            lay, bits = TQ_UNPACKED, 0
+            _gpu(self.idx, "keys.idx", torch.uint8)
+            _gpu(self.sign, "keys.sign", torch.int8)
+            _gpu(self.gamma, "keys.gamma", torch.float32)
+            row_i, row_s = D, D
+        elif self.layout == "packed":
+            lay, bits = TQ_PACKED, int(self.bits)
+            _gpu(self.idx, "keys.idx", torch.uint8)
+            _gpu(self.sign, "keys.sign", torch.uint8)
+            _gpu(self.gamma, "keys.gamma", torch.float16)
+            if bits not in (2, 3) or D % 8:
+                raise ValueError("packed keys need bits in (2, 3) and D % 8 == 0")
+            row_i, row_s = D * bits // 8, D // 8
+        else:
+            raise ValueError(f"unknown layout {self.layout!r}")
+        g = self.gamma if self.gamma.dim() == 2 else self.gamma.unsqueeze(0)
+        P, S = g.shape
+        if self.idx.numel() != P * S * row_i or self.sign.numel() != P * S * row_s:
+            raise ValueError(f"key streams do not match gamma's [P={P}, S={S}] with D={D}")
+        return _CKeys(lay, bits, self.idx.data_ptr(), self.sign.data_ptr(), self.gamma.data_ptr()), P, S
+
+    @property
+    def device(self) -> torch.device:
+        return self.gamma.device
+
+
+def _as3(t: torch.Tensor) -> torch.Tensor:
+    return t if t.dim() == 3 else t.unsqueeze(0)
+
+
+def tq_query_transform(q: torch.Tensor, Pi: torch.Tensor, S_mat: torch.Tensor,
+                       A: torch.Tensor | None = None, T: torch.Tensor | None = None,
+                       stream=None):
+    """A = Pi q and T = S_mat q. q [P,B,D] or [B,D]; Pi, S_mat [H,D,D] or [D,D]."""
+    squeeze = q.dim() == 2
+    q3 = _as3(_gpu(q, "q", torch.float32))
+    Pi3 = _as3(_gpu(Pi, "Pi", torch.float32))
+    S3 = _as3(_gpu(S_mat, "S_mat", torch.float32))
+    P, B, D = q3.shape
+    H = Pi3.shape[0]
+    if Pi3.shape != (H, D, D) or S3.shape != (H, D, D):
+        raise ValueError(f"Pi and S_mat must be [H, {D}, {D}]")
+    if A is None:
+        A = torch.empty_like(q3)
+    if T is None:
+        T = torch.empty_like(q3)
+    _gpu(A, "A", torch.float32)
+    _gpu(T, "T", torch.float32)
+    if A.numel() != q3.numel() or T.numel() != q3.numel():
+        raise ValueError("A and T must have q's shape")
+    st = _stream(q.device, stream)
+    _check(_lib.tq_query_transform(_ptr(q3), _ptr(Pi3), _ptr(S3), _ptr(A), _ptr(T),
+                                   P, H, B, D, st), "tq_query_transform")
+    if squeeze:
+        return A.view(B, D), T.view(B, D)
+    return A.view(P, B, D), T.view(P, B, D)
+
+
+def tq_score_with_kernel(A: torch.Tensor, T: torch.Tensor, keys: Keys, codebook: torch.Tensor,
+                         kernel: str = "auto", scores: torch.Tensor | None = None, stream=None):
+    """Raw scores [P,B,S] (or [B,S] for 2-D A) with an explicit kernel family."""
+    squeeze = A.dim() == 2
+    A3 = _as3(_gpu(A, "A", torch.float32))
+    T3 = _as3(_gpu(T, "T", torch.float32))
+    _gpu(codebook, "codebook", torch.float32)
+    if A3.shape != T3.shape:
+        raise ValueError("A and T must have the same shape")
+    P, B, D = A3.shape
+    ck, Pk, S = keys._c(D)
+    if Pk != P:
+        raise ValueError(f"keys hold {Pk} problems, A holds {P}")
+    if scores is None:
+        scores = torch.empty((P, B, S), dtype=torch.float32, device=A.device)
+    _gpu(scores, "scores", torch.float32)
+    if scores.numel() != P * B * S:
+        raise ValueError("scores must hold P*B*S floats")
+    st = _stream(A.device, stream)
+    _check(_lib.tq_score_with_kernel(_ptr(A3), _ptr(T3), ctypes.byref(ck), _ptr(codebook),
+                                     codebook.numel(), _ptr(scores), P, B, S, D,
+                                     KERNELS[kernel], st), "tq_score")
+    return scores.view(B, S) if squeeze else scores.view(P, B, S)
+
+
+def tq_score(A, T, keys: Keys, codebook, scores=None, stream=None):
+    """Raw scores [P,B,S] of transformed queries A, T against compressed keys."""
+    return tq_score_with_kernel(A, T, keys, codebook, "auto", scores, stream)
+
+
+def tq_score_kernel_name(layout: str, bits: int, C: int, B: int, D: int, kernel: str = "auto"):
+    lay = TQ_UNPACKED if layout == "unpacked" else TQ_PACKED
+    name = _lib.tq_score_kernel_name(lay, int(bits), int(C), int(B), int(D), KERNELS[kernel])
+    return None if name is None else name.decode()
+
+
+def tq_decode_debug(keys: Keys, D: int, stream=None):
+    """Expand keys to (idx uint8 [P,S,D], sign int8 [P,S,D], gamma float32 [P,S])."""
+    ck, P, S = keys._c(D)
+    dev = keys.device
+    idx = torch.empty((P, S, D), dtype=torch.uint8, device=dev)
+    sign = torch.empty((P, S, D), dtype=torch.int8, device=dev)
+    gamma = torch.empty((P, S), dtype=torch.float32, device=dev)
+    st = _stream(dev, stream)
+    _check(_lib.tq_decode_debug(ctypes.byref(ck), _ptr(idx), _ptr(sign), _ptr(gamma),
+                                P, S, D, st), "tq_decode_debug")
+    return idx, sign, gamma

@@ -1,0 +1,150 @@
+// C ABI of the scoring library: argument validation and kernel dispatch.
+// Every check runs on the host before any launch; see include/tq.h for the
+// contract of each entry point.
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_common.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Products of sizes stay far below 2^62 for any input that fits in memory,
+// but reject shapes whose element counts would not fit int64 arithmetic.
+bool fits(int64_t a, int64_t b, int64_t c) {
+    const int64_t lim = (int64_t)1 << 60;
+    if (a > lim / b) return false;
+    return a * b <= lim / c;
+}
+
+// Format checks that do not depend on the buffers.
+int check_format(const tq_keys* keys, int C, int D, bool need_c) {
+    if (!keys) return TQ_ERR_ARG;
+    if (D <= 0) return TQ_ERR_ARG;
+    if (keys->layout != TQ_UNPACKED && keys->layout != TQ_PACKED) return TQ_ERR_ARG;
+    if (D > TQ_MAX_D) return TQ_ERR_UNSUPPORTED;
+    if (keys->layout == TQ_PACKED) {
+        if (keys->bits != 2 && keys->bits != 3) return TQ_ERR_UNSUPPORTED;
+        if (D % 8 != 0) return TQ_ERR_UNSUPPORTED;
+        if (need_c && C != (1 << keys->bits)) return TQ_ERR_UNSUPPORTED;
+    } else if (need_c && (C < 1 || C > 256)) {
+        return TQ_ERR_UNSUPPORTED;
+    }
+    return TQ_OK;
+}
+
+// Buffer checks for a non-empty call.
+int check_buffers(const tq_keys* keys, int P, int S, int D) {
+    if (!keys->idx || !keys->sign || !keys->gamma) return TQ_ERR_ARG;
+    if (P > 65535) return TQ_ERR_UNSUPPORTED;
+    if (!fits(P, S, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(keys->idx) || !aligned16(keys->sign) || !aligned16(keys->gamma)) return TQ_ERR_ALIGN;
+    return TQ_OK;
+}
+
+tq::KeyStreams streams(const tq_keys* k) {
+    return tq::KeyStreams{static_cast<const uint8_t*>(k->idx), static_cast<const uint8_t*>(k->sign),
+                          k->gamma};
+}
+
+bool mfma_ok(int layout, int bits, int C, int B, int D) {
+    return tq::score_mfma_supported(layout, layout == TQ_PACKED ? bits : 0, C, B, D);
+}
+
+// Default choice: the matrix-core family wherever it applies, the vector
+// family for everything else (odd D, codebooks over 8 entries).
+int pick_kernel(int layout, int bits, int C, int B, int D) {
+    return mfma_ok(layout, bits, C, B, D) ? TQ_KERNEL_MFMA : TQ_KERNEL_VALU;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(int status) {
+    switch (status) {
+        case TQ_OK: return "ok";
+        case TQ_ERR_ARG: return "invalid argument (null pointer, negative size, D or H not positive, P % H != 0, unknown layout or kernel)";
+        case TQ_ERR_UNSUPPORTED: return "unsupported shape or key format";
+        case TQ_ERR_ALIGN: return "a buffer is not 16-byte aligned";
+        case TQ_ERR_LAUNCH: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int tq_query_transform(const float* q, const float* Pi, const float* S_mat, float* A, float* T,
+                       int P, int H, int B, int D, void* stream) {
+    if (P < 0 || H <= 0 || B < 0 || D <= 0 || P % H != 0) return TQ_ERR_ARG;
+    if (D > TQ_MAX_D) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!q || !Pi || !S_mat || !A || !T) return TQ_ERR_ARG;
+    if (D > TQ_MAX_D || P > 65535 || !fits(P, B, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(Pi) || !aligned16(S_mat) || !aligned16(A) || !aligned16(T))
+        return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_query_transform(q, Pi, S_mat, A, T, P, H, B, D,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+const char* tq_score_kernel_name(int layout, int bits, int C, int B, int D, int kernel) {
+    if (layout != TQ_UNPACKED && layout != TQ_PACKED) return nullptr;
+    if (B <= 0 || D <= 0 || D > TQ_MAX_D) return nullptr;
+    if (layout == TQ_PACKED && ((bits != 2 && bits != 3) || D % 8 || C != (1 << bits))) return nullptr;
+    if (layout == TQ_UNPACKED && (C < 1 || C > 256)) return nullptr;
+    if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(layout, bits, C, B, D);
+    if (kernel == TQ_KERNEL_MFMA)
+        return tq::score_mfma_name(layout, layout == TQ_PACKED ? bits : 0, C, B, D);
+    if (kernel == TQ_KERNEL_VALU)
+        return layout == TQ_UNPACKED ? "valu_unpacked" : bits == 2 ? "valu_packed2" : "valu_packed3";
+    return nullptr;
+}
+
+int tq_score_with_kernel(const float* A, const float* T, const tq_keys* keys, const float* codebook,
+                         int C, float* scores, int P, int B, int S, int D, int kernel, void* stream) {
+    if (P < 0 || B < 0 || S < 0) return TQ_ERR_ARG;
+    int kc = check_format(keys, C, D, true);
+    if (kc != TQ_OK) return kc;
+    if (kernel != TQ_KERNEL_AUTO && kernel != TQ_KERNEL_VALU && kernel != TQ_KERNEL_MFMA) return TQ_ERR_ARG;
+    if (P == 0 || B == 0 || S == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!A || !T || !codebook || !scores) return TQ_ERR_ARG;
+    kc = check_buffers(keys, P, S, D);
+    if (kc != TQ_OK) return kc;
+    if (B > 262144 || !fits(P, B, S) || !fits(P, B, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(A) || !aligned16(T) || !aligned16(codebook) || !aligned16(scores)) return TQ_ERR_ALIGN;
+    const int bits = keys->layout == TQ_PACKED ? keys->bits : 0;
+    if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(keys->layout, bits, C, B, D);
+    hipError_t e;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (kernel == TQ_KERNEL_MFMA) {
+        if (!mfma_ok(keys->layout, bits, C, B, D)) return TQ_ERR_UNSUPPORTED;
+        e = tq::launch_score_mfma(A, T, streams(keys), keys->layout, bits, codebook, C, scores, P, B, S, D, st);
+    } else if (kernel == TQ_KERNEL_VALU) {
+        e = tq::launch_score_valu(A, T, streams(keys), keys->layout, bits, codebook, C, scores, P, B, S, D, st);
+    } else {
+        return TQ_ERR_ARG;
+    }
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_score(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
+             float* scores, int P, int B, int S, int D, void* stream) {
+    return tq_score_with_kernel(A, T, keys, codebook, C, scores, P, B, S, D, TQ_KERNEL_AUTO, stream);
+}
+
+int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
+                    int P, int S, int D, void* stream) {
+    if (P < 0 || S < 0) return TQ_ERR_ARG;
+    int kc = check_format(keys, 0, D, false);
+    if (kc != TQ_OK) return kc;
+    if (P == 0 || S == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!idx_out || !sign_out || !gamma_out) return TQ_ERR_ARG;
+    kc = check_buffers(keys, P, S, D);
+    if (kc != TQ_OK) return kc;
+    if (!aligned16(idx_out) || !aligned16(sign_out) || !aligned16(gamma_out)) return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_decode(streams(keys), keys->layout, keys->bits, idx_out, sign_out,
+                                           gamma_out, P, S, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+}  // extern "C"

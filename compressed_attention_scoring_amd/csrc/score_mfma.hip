@@ -1,0 +1,666 @@
+// Scoring kernel, matrix-core family (CDNA4 v_mfma_f32_32x32x16_f16).
+//
+// What it computes is the scoring identity of "TurboQuant Attention in CUDA:
+// Transform the Query, Reuse the Work" (sections "Move the transforms to the
+// query", "Two kernels, two jobs"):
+//   scores[b,s] = M[b,s] + (sqrt(pi/2)/D) gamma_s R[b,s],
+//   M = A C^T with C[s,d] = codebook[idx[s,d]],  R = T Sigma^T with Sigma = signs.
+// Both M and R are dense contractions over D across a block of queries, so they
+// run on the matrix cores: queries are the 32 MFMA rows, keys the 32 columns,
+// coordinates the contraction. "Fitting 4.4x More Context on Jetson", section
+// "v5: Extended 2D SDPA", writes the same score as one inner product of length
+// 2D; here the two halves keep separate accumulators because gamma_s scales
+// only the second.
+//
+// fp32 accuracy from f16 matrix cores. Each fp32 operand x is split into
+// x_hi = f16(x) and x_lo = f16(x - x_hi) (after a power-of-two scale that keeps
+// both in f16 range), giving 22 significant bits; products of f16 pairs are
+// exact in the fp32 accumulator. Signs are exactly +-1 in f16. Five products
+// per k-step: A_hi c_hi, A_lo c_hi, A_hi c_lo (the dropped A_lo c_lo is below
+// 2^-22 relative) into M, and T_hi sigma, T_lo sigma into R.
+//
+// Data flow per workgroup (4 wavefronts):
+//  * prologue: the query-side operands A_hi, A_lo, T_hi, T_lo of up to MT
+//    32-query tiles are built once from fp32 A and T and stored in LDS in the
+//    exact per-lane operand order, so the main loop reads them with one
+//    conflict-free 16-byte LDS read per operand;
+//  * main loop: each wavefront takes 32-key tiles. A lane owns one key
+//    (column lane % 32) and one half of its coordinates (lane / 32), loads that
+//    half's index and sign bytes with wide loads, and builds its key-side
+//    operands in registers: byte-select (v_perm) lookups into the codebook's
+//    f16 hi/lo byte tables, and sign bits moved into the f16 sign position of
+//    1.0. Nothing is gathered from memory ("Fitting 4.4x More Context on
+//    Jetson", section "Can TurboQuant Match Scaled Dot-Product Attention?",
+//    found the per-coordinate centroid gather to be its largest cost);
+//  * epilogue: scores = M * (1/(sA sc)) + (coef/sT) gamma R, written as full
+//    128-byte rows of consecutive keys.
+//
+// The order in which a lane's coordinates enter the contraction is free (the
+// query-side operands are built in the same order), so each key layout uses the
+// order in which its bitstream unpacks with the fewest instructions; see
+// mse_dim and qjl_dim.
+#include "tq_common.hpp"
+
+namespace tq {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTileKeys = 32;
+constexpr uint32_t kOneOne = 0x3C003C00u;   // two f16 1.0
+constexpr uint32_t kSignBits = 0x80008000u;
+
+union Op8 {
+    f16x8 h;
+    uint32_t u[4];
+};
+
+// ---------------------------------------------------------------------------
+// Coordinate order. Element e (0..7) of k-step j of a lane half covers
+// coordinate half_base + mse_dim(j, e) in the codebook contraction and
+// half_base + qjl_dim(j, e) in the sign contraction.
+// ---------------------------------------------------------------------------
+
+// 3-bit fields t of a 24-bit group taken per k-step (four k-steps per 32
+// coordinates): fields that sit inside one byte first, the two that straddle a
+// byte boundary (t = 2, 5) last.
+__host__ __device__ constexpr int t3_field(int jj, int hi) {
+    return jj == 0 ? (hi ? 1 : 0) : jj == 1 ? (hi ? 4 : 3) : jj == 2 ? (hi ? 7 : 6) : (hi ? 5 : 2);
+}
+
+template <int LAYOUT, int BITS>
+__host__ __device__ constexpr int mse_dim(int j, int e) {
+    if (LAYOUT == 0) return 8 * j + e;
+    if (BITS == 2) return 16 * (j / 2) + 4 * (e % 4) + 2 * (j % 2) + e / 4;
+    // BITS == 3: 32-coordinate blocks of four 24-bit groups m = 0..3
+    const int blk = j / 4, jj = j % 4, pos = e % 4;
+    const int t = t3_field(jj, e >= 4);
+    const int m = (jj == 3) ? (pos == 1 ? 2 : pos == 2 ? 1 : pos) : pos;
+    return 32 * blk + 8 * m + t;
+}
+
+template <int LAYOUT>
+__host__ __device__ constexpr int qjl_dim(int j, int e) {
+    if (LAYOUT == 0) return 8 * j + ((e & 4) | ((e & 1) << 1) | ((e >> 1) & 1));
+    return 32 * (j / 4) + 4 * (j % 4) + e / 2 + 16 * (e % 2);
+}
+
+// Inverses: the k-step j and element e that coordinate dd (within a lane half)
+// occupies in each contraction.
+template <int LAYOUT, int BITS>
+__host__ __device__ constexpr void mse_slot(int dd, int& j, int& e) {
+    if (LAYOUT == 0) {
+        j = dd / 8;
+        e = dd % 8;
+    } else if (BITS == 2) {
+        const int r = dd % 16;
+        e = r / 4 + 4 * (r % 2);
+        j = 2 * (dd / 16) + (r % 4) / 2;
+    } else {
+        const int blk = dd / 32, m = (dd % 32) / 8, t = dd % 8;
+        const int jj = (t == 0 || t == 1) ? 0 : (t == 3 || t == 4) ? 1 : (t == 6 || t == 7) ? 2 : 3;
+        const int hi = (t == 1 || t == 4 || t == 7 || t == 5) ? 1 : 0;
+        const int pos = (jj == 3) ? (m == 1 ? 2 : m == 2 ? 1 : m) : m;
+        e = pos + 4 * hi;
+        j = 4 * blk + jj;
+    }
+}
+
+template <int LAYOUT>
+__host__ __device__ constexpr void qjl_slot(int dd, int& j, int& e) {
+    if (LAYOUT == 0) {
+        const int r = dd % 8;
+        e = (r & 4) | ((r & 1) << 1) | ((r >> 1) & 1);   // the order is its own inverse
+        j = dd / 8;
+    } else {
+        const int r = dd % 32, r2 = r % 16;
+        e = 2 * (r2 % 4) + r / 16;
+        j = 4 * (dd / 32) + r2 / 4;
+    }
+}
+
+// The same slots for coordinate dd = 16*blk16 + k, written so that with k a
+// compile-time constant only a few operations on blk16 remain at run time.
+template <int LAYOUT, int BITS>
+__host__ __device__ constexpr void mse_slot16(int blk16, int k, int& j, int& e) {
+    if (LAYOUT == 0) {
+        j = 2 * blk16 + k / 8;
+        e = k % 8;
+    } else if (BITS == 2) {
+        e = k / 4 + 4 * (k % 2);
+        j = 2 * blk16 + (k % 4) / 2;
+    } else {
+        const int h = blk16 & 1, t = k % 8;
+        const int jj = (t == 0 || t == 1) ? 0 : (t == 3 || t == 4) ? 1 : (t == 6 || t == 7) ? 2 : 3;
+        const int hi = (t == 1 || t == 4 || t == 7 || t == 5) ? 1 : 0;
+        const int pos = (jj == 3) ? 2 * (k / 8) + h : 2 * h + k / 8;
+        e = pos + 4 * hi;
+        j = 4 * (blk16 >> 1) + jj;
+    }
+}
+
+template <int LAYOUT>
+__host__ __device__ constexpr void qjl_slot16(int blk16, int k, int& j, int& e) {
+    if (LAYOUT == 0) {
+        const int r = k % 8;
+        e = (r & 4) | ((r & 1) << 1) | ((r >> 1) & 1);
+        j = 2 * blk16 + k / 8;
+    } else {
+        e = 2 * (k % 4) + (blk16 & 1);
+        j = 4 * (blk16 >> 1) + k / 4;
+    }
+}
+
+template <int LAYOUT, int BITS, int HALF>
+constexpr bool slot16_matches() {
+    for (int dd = 0; dd < HALF; ++dd) {
+        int j1 = 0, e1 = 0, j2 = 0, e2 = 0;
+        mse_slot<LAYOUT, BITS>(dd, j1, e1);
+        mse_slot16<LAYOUT, BITS>(dd / 16, dd % 16, j2, e2);
+        if (j1 != j2 || e1 != e2) return false;
+        qjl_slot<LAYOUT>(dd, j1, e1);
+        qjl_slot16<LAYOUT>(dd / 16, dd % 16, j2, e2);
+        if (j1 != j2 || e1 != e2) return false;
+    }
+    return true;
+}
+static_assert(slot16_matches<0, 0, 16>() && slot16_matches<0, 0, 128>() && slot16_matches<1, 2, 32>() &&
+              slot16_matches<1, 2, 128>() && slot16_matches<1, 3, 32>() && slot16_matches<1, 3, 128>(),
+              "block-split slots");
+
+// Compile-time proof that every coordinate of a lane half lands in exactly one
+// (k-step, element) slot of each contraction and that the slot maps invert.
+template <int LAYOUT, int BITS, int HALF>
+constexpr bool orders_are_bijections() {
+    for (int j = 0; j < HALF / 8; ++j) {
+        for (int e = 0; e < 8; ++e) {
+            int j2 = -1, e2 = -1;
+            const int dm = mse_dim<LAYOUT, BITS>(j, e);
+            if (dm < 0 || dm >= HALF) return false;
+            mse_slot<LAYOUT, BITS>(dm, j2, e2);
+            if (j2 != j || e2 != e) return false;
+            const int dq = qjl_dim<LAYOUT>(j, e);
+            if (dq < 0 || dq >= HALF) return false;
+            qjl_slot<LAYOUT>(dq, j2, e2);
+            if (j2 != j || e2 != e) return false;
+        }
+    }
+    return true;
+}
+static_assert(orders_are_bijections<0, 0, 16>() && orders_are_bijections<0, 0, 32>() &&
+              orders_are_bijections<0, 0, 64>() && orders_are_bijections<0, 0, 128>(), "unpacked orders");
+static_assert(orders_are_bijections<1, 2, 32>() && orders_are_bijections<1, 2, 64>() &&
+              orders_are_bijections<1, 2, 128>(), "2-bit orders");
+static_assert(orders_are_bijections<1, 3, 32>() && orders_are_bijections<1, 3, 64>() &&
+              orders_are_bijections<1, 3, 128>(), "3-bit orders");
+
+// ---------------------------------------------------------------------------
+// Key-side operand builders
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+// Four selector bytes (each < 8) -> two dwords of f16 pairs from a byte table
+// tab = {low bytes of entries 0-3, low bytes of 4-7, high bytes of 0-3, high bytes of 4-7}.
+__device__ __forceinline__ void lut4(uint32_t x, const uint32_t (&tab)[4], uint32_t& o0, uint32_t& o1) {
+    const uint32_t lo = perm(tab[1], tab[0], x);
+    const uint32_t hi = perm(tab[3], tab[2], x);
+    o0 = perm(hi, lo, 0x05010400u);
+    o1 = perm(hi, lo, 0x07030602u);
+}
+
+template <int LAYOUT, int BITS>
+struct Fmt;
+
+template <>
+struct Fmt<0, 0> {   // unpacked: one byte per index and per sign
+    template <int D> static constexpr int idx_dw() { return D / 8; }   // per lane half
+    template <int D> static constexpr int sign_dw() { return D / 8; }
+    template <int D> static constexpr int idx_row() { return D; }
+    template <int D> static constexpr int sign_row() { return D; }
+    template <int NI>
+    __device__ static __forceinline__ void selectors(const uint32_t (&w)[NI], int j, uint32_t& x0, uint32_t& x1) {
+        x0 = w[2 * j];
+        x1 = w[2 * j + 1];
+    }
+    template <int NS>
+    __device__ static __forceinline__ void signs(const uint32_t (&s)[NS], int j, uint32_t (&o)[4]) {
+        const uint32_t s0 = s[2 * j], s1 = s[2 * j + 1];
+        o[0] = ((s0 << 8) & kSignBits) | kOneOne;   // coordinates 0, 2
+        o[1] = (s0 & kSignBits) | kOneOne;          // coordinates 1, 3
+        o[2] = ((s1 << 8) & kSignBits) | kOneOne;   // coordinates 4, 6
+        o[3] = (s1 & kSignBits) | kOneOne;          // coordinates 5, 7
+    }
+};
+
+// packed sign stream: bit 1 = +1; the f16 sign bit must be set for bit 0
+template <int NS>
+__device__ __forceinline__ void packed_signs(const uint32_t (&s)[NS], int j, uint32_t (&o)[4]) {
+    const uint32_t nv = ~s[j / 4];
+    const int k0 = 4 * (j % 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = ((nv << (15 - (k0 + i))) & kSignBits) | kOneOne;
+}
+
+template <>
+struct Fmt<1, 2> {   // 2-bit indices, 16 per dword
+    template <int D> static constexpr int idx_dw() { return D / 32; }
+    template <int D> static constexpr int sign_dw() { return D / 64; }
+    template <int D> static constexpr int idx_row() { return D / 4; }
+    template <int D> static constexpr int sign_row() { return D / 8; }
+    template <int NI>
+    __device__ static __forceinline__ void selectors(const uint32_t (&w)[NI], int j, uint32_t& x0, uint32_t& x1) {
+        const uint32_t v = w[j / 2];
+        const int k0 = 2 * (j % 2);
+        x0 = (v >> (2 * k0)) & 0x03030303u;
+        x1 = (v >> (2 * k0 + 2)) & 0x03030303u;
+    }
+    template <int NS>
+    __device__ static __forceinline__ void signs(const uint32_t (&s)[NS], int j, uint32_t (&o)[4]) {
+        packed_signs(s, j, o);
+    }
+};
+
+template <>
+struct Fmt<1, 3> {   // 3-bit indices, 32 per three dwords
+    template <int D> static constexpr int idx_dw() { return 3 * D / 64; }
+    template <int D> static constexpr int sign_dw() { return D / 64; }
+    template <int D> static constexpr int idx_row() { return 3 * D / 8; }
+    template <int D> static constexpr int sign_row() { return D / 8; }
+    template <int NI>
+    __device__ static __forceinline__ void selectors(const uint32_t (&w)[NI], int j, uint32_t& x0, uint32_t& x1) {
+        const uint32_t W0 = w[3 * (j / 4)], W1 = w[3 * (j / 4) + 1], W2 = w[3 * (j / 4) + 2];
+        constexpr uint32_t m = 0x07070707u, m2 = 0x00070007u;
+        switch (j % 4) {
+            case 0: {   // fields 0 and 1 of groups 0..3: bytes 0, 3, 6, 9 at bit offsets 0 and 3
+                const uint32_t g = perm(W1, W0, 0x0C0C0300u) | perm(W2, W1, 0x05020C0Cu);
+                x0 = g & m;
+                x1 = (g >> 3) & m;
+                break;
+            }
+            case 1: {   // fields 3 and 4: bytes 1, 4, 7, 10 at offsets 1 and 4
+                const uint32_t g = perm(W1, W0, 0x0C0C0401u) | perm(W2, W1, 0x06030C0Cu);
+                x0 = (g >> 1) & m;
+                x1 = (g >> 4) & m;
+                break;
+            }
+            case 2: {   // fields 6 and 7: bytes 2, 5, 8, 11 at offsets 2 and 5
+                const uint32_t g = perm(W1, W0, 0x0C0C0502u) | perm(W2, W1, 0x07040C0Cu);
+                x0 = (g >> 2) & m;
+                x1 = (g >> 5) & m;
+                break;
+            }
+            default: {  // fields 2 and 5 straddle bytes: 16-bit windows, groups in order 0, 2, 1, 3
+                const uint32_t a = perm(W1, W0, 0x04030100u);   // bytes 0,1 | 3,4
+                const uint32_t b = perm(W2, W1, 0x06050302u);   // bytes 6,7 | 9,10
+                x0 = ((a >> 6) & m2) | (((b >> 6) & m2) << 8);
+                const uint32_t c = perm(W1, W0, 0x05040201u);   // bytes 1,2 | 4,5
+                const uint32_t d = perm(W2, W1, 0x07060403u);   // bytes 7,8 | 10,11
+                x1 = ((c >> 7) & m2) | (((d >> 7) & m2) << 8);
+                break;
+            }
+        }
+    }
+    template <int NS>
+    __device__ static __forceinline__ void signs(const uint32_t (&s)[NS], int j, uint32_t (&o)[4]) {
+        packed_signs(s, j, o);
+    }
+};
+
+// Load N dwords from an address aligned to ALIGN bytes (4, 8 or 16), using the
+// widest loads that alignment allows.
+template <int N, int ALIGN>
+__device__ __forceinline__ void load_dwords(const uint8_t* __restrict__ p, uint32_t (&v)[N]) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    int i = 0;
+    if constexpr (ALIGN % 16 == 0) {
+#pragma unroll
+        for (; i + 4 <= N; i += 4) {
+            const uint4 t = *reinterpret_cast<const uint4*>(q + i);
+            v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+        }
+    }
+    if constexpr (ALIGN % 8 == 0) {
+#pragma unroll
+        for (; i + 2 <= N; i += 2) {
+            const uint2 t = *reinterpret_cast<const uint2*>(q + i);
+            v[i] = t.x; v[i + 1] = t.y;
+        }
+    }
+#pragma unroll
+    for (; i < N; ++i) v[i] = q[i];
+}
+
+constexpr int align_of_half(int row_bytes) {
+    // lane halves start at key * row + (0 or row / 2) from a 16-byte aligned base
+    return (row_bytes / 2) % 16 == 0 ? 16 : (row_bytes / 2) % 8 == 0 ? 8 : 4;
+}
+
+__device__ __forceinline__ float pow2_scale_for(float maxabs) {
+    // a power of two bringing maxabs into [2^13, 2^14); 1 if maxabs is 0 or not finite
+    if (!(maxabs > 0.f) || !(maxabs < 3.0e38f)) return 1.f;
+    int e;
+    (void)frexpf(maxabs, &e);   // maxabs = f * 2^e, f in [0.5, 1)
+    return ldexpf(1.f, 14 - e);
+}
+
+__device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
+    const _Float16 h = (_Float16)x;
+    const _Float16 l = (_Float16)(x - (float)h);
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// One 32-key tile's compressed codes for this lane: its key's half of the index
+// and sign streams, and the key's gamma.
+template <int NI, int NS>
+struct TileCodes {
+    uint32_t iw[NI];
+    uint32_t sw[NS];
+    float gam;
+};
+
+template <int LAYOUT, int BITS, int D>
+__device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
+                                                    Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
+                                          const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+                                          const void* __restrict__ gamma, int64_t key, int g) {
+    using F = Fmt<LAYOUT, BITS>;
+    constexpr int NI = F::template idx_dw<D>();
+    constexpr int NS = F::template sign_dw<D>();
+    constexpr int IDX_ROW = F::template idx_row<D>();
+    constexpr int SIGN_ROW = F::template sign_row<D>();
+    load_dwords<NI, align_of_half(IDX_ROW)>(idx + key * IDX_ROW + g * (IDX_ROW / 2), c.iw);
+    load_dwords<NS, align_of_half(SIGN_ROW)>(sign + key * SIGN_ROW + g * (SIGN_ROW / 2), c.sw);
+    if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
+    else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
+}
+
+template <int LAYOUT, int BITS, int D, int MT>
+__global__ __launch_bounds__(kThreads) void score_mfma_kernel(
+    const float* __restrict__ A, const float* __restrict__ T,
+    const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+    const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
+    float* __restrict__ scores, int B, int S, float coef) {
+    using F = Fmt<LAYOUT, BITS>;
+    constexpr int KS = D / 16;                 // k-steps (16 coordinates each)
+    constexpr int HALF = D / 2;                // coordinates per lane half
+    constexpr int NI = F::template idx_dw<D>();
+    constexpr int NS = F::template sign_dw<D>();
+    constexpr int BLOCK = 64 * 16;             // one operand block: 64 lanes x 16 bytes
+    constexpr int OPS_BYTES = MT * KS * 4 * BLOCK;
+    constexpr int SEG = 16;                    // coordinates each prologue lane converts
+    constexpr int PER_ROW = D / SEG;           // prologue lanes per query row
+    constexpr int ROWS_PER_PASS = kThreads / PER_ROW;
+
+    __shared__ __attribute__((aligned(16))) uint8_t ops[OPS_BYTES];
+    __shared__ float2 rowk[MT * 32];           // per-row epilogue factors (M, R)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int p = blockIdx.z;
+    const int b0 = blockIdx.y * MT * 32;
+    const int rows = min(MT * 32, B - b0);
+    const int col = lane & 31;
+    const int g = lane >> 5;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    const int stride = gridDim.x * kWaves;
+    const int64_t key0 = (int64_t)p * S;
+
+    // ---- the first tile's codes are requested before anything else, so the
+    //      HBM latency overlaps building the query-side operands
+    int tile = blockIdx.x * kWaves + wave;
+    TileCodes<NI, NS> cur;
+    if (tile < ntiles) {
+        const int s = min(tile * kTileKeys + col, S - 1);
+        load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
+    }
+
+    // ---- codebook: power-of-two scale, f16 hi/lo split, byte tables for v_perm
+    float cbv[8];
+    float mc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        cbv[k] = k < C ? codebook[k] : 0.f;
+        mc = fmaxf(mc, fabsf(cbv[k]));
+    }
+    const float sc = pow2_scale_for(mc);
+    uint32_t tab_hi[4] = {0u, 0u, 0u, 0u}, tab_lo[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        uint16_t hb, lb;
+        split_f16(cbv[k] * sc, hb, lb);
+        const int w = k >> 2, sh = 8 * (k & 3);
+        tab_hi[w] |= (uint32_t)(hb & 0xffu) << sh;
+        tab_hi[2 + w] |= (uint32_t)(hb >> 8) << sh;
+        tab_lo[w] |= (uint32_t)(lb & 0xffu) << sh;
+        tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
+    }
+
+    // ---- query-side operands: each row of A and T is scaled by its own power of
+    //      two (row max found by the 8 lanes that hold the row), split into f16
+    //      hi/lo and stored at the slot its coordinate occupies in the operands
+    const float* Ap = A + ((int64_t)p * B + b0) * D;
+    const float* Tp = T + ((int64_t)p * B + b0) * D;
+    for (int r0 = 0; r0 < MT * 32; r0 += ROWS_PER_PASS) {
+        const int row = r0 + tid / PER_ROW;            // row within this workgroup's tiles
+        const int part = tid % PER_ROW;                // coordinates 16*part .. 16*part+15
+        float a[SEG], t[SEG];
+        float ma = 0.f, mt = 0.f;
+        if (row < rows) {
+#pragma unroll
+            for (int k = 0; k < SEG; k += 4) {
+                const float4 va = *reinterpret_cast<const float4*>(Ap + (int64_t)row * D + part * SEG + k);
+                const float4 vt = *reinterpret_cast<const float4*>(Tp + (int64_t)row * D + part * SEG + k);
+                a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
+                t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < SEG; ++k) a[k] = t[k] = 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < SEG; ++k) {
+            ma = fmaxf(ma, fabsf(a[k]));
+            mt = fmaxf(mt, fabsf(t[k]));
+        }
+#pragma unroll
+        for (int o = 1; o < PER_ROW; o <<= 1) {
+            ma = fmaxf(ma, __shfl_xor(ma, o));
+            mt = fmaxf(mt, __shfl_xor(mt, o));
+        }
+        const float sA = pow2_scale_for(ma);
+        const float sT = pow2_scale_for(mt);
+        if (row < MT * 32 && part == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
+        if (row < MT * 32) {
+            const int mtile = row / 32, rl = row % 32;
+            const int gg = (part * SEG) / HALF;                 // lane half holding these coordinates
+            const int blk16 = ((part * SEG) % HALF) / SEG;      // their 16-coordinate block in the half
+            uint8_t* lane_base = ops + (mtile * KS * 4) * BLOCK + (gg * 32 + rl) * 16;
+#pragma unroll
+            for (int k = 0; k < SEG; ++k) {
+                uint16_t hi, lo;
+                int j, e;
+                mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
+                split_f16(a[k] * sA, hi, lo);
+                uint8_t* base = lane_base + (j * 4) * BLOCK + e * 2;
+                *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = hi;
+                *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = lo;
+                qjl_slot16<LAYOUT>(blk16, k, j, e);
+                split_f16(t[k] * sT, hi, lo);
+                base = lane_base + (j * 4) * BLOCK + e * 2;
+                *reinterpret_cast<uint16_t*>(base + 2 * BLOCK) = hi;
+                *reinterpret_cast<uint16_t*>(base + 3 * BLOCK) = lo;
+            }
+        }
+    }
+    __syncthreads();
+
+    float* out_p = scores + ((int64_t)p * B + b0) * S;
+
+    while (tile < ntiles) {
+        const int next = tile + stride;
+        TileCodes<NI, NS> nxt;
+        if (next < ntiles) {   // prefetch the next tile while this one is computed
+            const int s = min(next * kTileKeys + col, S - 1);
+            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma, key0 + s, g);
+        }
+
+        f32x16 accM[MT], accR[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { accM[mt][v] = 0.f; accR[mt][v] = 0.f; }
+        }
+
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            uint32_t x0, x1;
+            F::template selectors<NI>(cur.iw, j, x0, x1);
+            Op8 chi, clo, sg;
+            lut4(x0, tab_hi, chi.u[0], chi.u[1]);
+            lut4(x1, tab_hi, chi.u[2], chi.u[3]);
+            lut4(x0, tab_lo, clo.u[0], clo.u[1]);
+            lut4(x1, tab_lo, clo.u[2], clo.u[3]);
+            F::template signs<NS>(cur.sw, j, sg.u);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t* base = ops + ((mt * KS + j) * 4) * BLOCK + lane * 16;
+                Op8 ahi, alo, thi, tlo;
+                *reinterpret_cast<uint4*>(ahi.u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
+                *reinterpret_cast<uint4*>(alo.u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
+                *reinterpret_cast<uint4*>(thi.u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
+                *reinterpret_cast<uint4*>(tlo.u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
+                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi.h, chi.h, accM[mt], 0, 0, 0);
+                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi.h, sg.h, accR[mt], 0, 0, 0);
+                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo.h, chi.h, accM[mt], 0, 0, 0);
+                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo.h, sg.h, accR[mt], 0, 0, 0);
+                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi.h, clo.h, accM[mt], 0, 0, 0);
+            }
+            // keep each k-step's operands live only for that step
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        const int s = tile * kTileKeys + col;
+        if (s < S) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+                    if (row < rows) {
+                        const float2 k = rowk[row];
+                        out_p[(int64_t)row * S + s] = fmaf(k.y * cur.gam, accR[mt][v], accM[mt][v] * k.x);
+                    }
+                }
+            }
+        }
+        cur = nxt;
+        tile = next;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side: shape support and launch
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxLdsBytes = 128 * 1024;
+
+int mt_for(int B, int D) {
+    const int tiles = (B + 31) / 32;
+    const int per_tile = (D / 16) * 4 * 1024;        // LDS bytes per 32-query tile
+    int cap = kMaxLdsBytes / per_tile;
+    if (cap > 4) cap = 4;
+    if (cap < 1) cap = 1;
+    if (tiles >= 4 && cap >= 4) return 4;
+    if (tiles >= 2 && cap >= 2) return 2;
+    return 1;
+}
+
+template <int LAYOUT, int BITS, int D, int MT>
+hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                     float* scores, int P, int B, int S, hipStream_t stream) {
+    const int groups = (B + MT * 32 - 1) / (MT * 32);
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    const int per_tile = (D / 16) * 4 * 1024 * MT;
+    int resident = (160 * 1024) / (per_tile + 64);   // workgroups a CU can hold by LDS
+    if (resident > 8) resident = 8;
+    if (resident < 1) resident = 1;
+    const int64_t target = 256LL * resident;            // 256 compute units
+    int64_t gx = (ntiles + kWaves - 1) / kWaves;
+    const int64_t others = (int64_t)groups * P;
+    int64_t cap = target / others;
+    if (cap < 1) cap = 1;
+    if (gx > cap) gx = cap;
+    const float coef = (float)(kSqrtHalfPi / (double)D);
+    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT>), dim3((unsigned)gx, groups, P),
+                       dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
+                       scores, B, S, coef);
+    return hipGetLastError();
+}
+
+template <int LAYOUT, int BITS, int D>
+hipError_t launch_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                    float* scores, int P, int B, int S, hipStream_t stream) {
+    switch (mt_for(B, D)) {
+        case 4:
+            if constexpr (D <= 128)
+                return launch_mt<LAYOUT, BITS, D, 4>(A, T, k, codebook, C, scores, P, B, S, stream);
+            [[fallthrough]];
+        case 2:
+            return launch_mt<LAYOUT, BITS, D, 2>(A, T, k, codebook, C, scores, P, B, S, stream);
+        default:
+            return launch_mt<LAYOUT, BITS, D, 1>(A, T, k, codebook, C, scores, P, B, S, stream);
+    }
+}
+
+template <int LAYOUT, int BITS>
+hipError_t launch_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
+                         int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
+    switch (D) {
+        case 32:
+            if constexpr (LAYOUT == 0)
+                return launch_d<LAYOUT, BITS, 32>(A, T, k, codebook, C, scores, P, B, S, stream);
+            break;
+        case 64: return launch_d<LAYOUT, BITS, 64>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 128: return launch_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 256: return launch_d<LAYOUT, BITS, 256>(A, T, k, codebook, C, scores, P, B, S, stream);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool score_mfma_supported(int layout, int bits, int C, int B, int D) {
+    (void)B;
+    if (C < 1 || C > 8) return false;          // byte-select lookup tables hold 8 entries
+    if (layout == 0) return D == 32 || D == 64 || D == 128 || D == 256;
+    if (bits != 2 && bits != 3) return false;
+    return D == 64 || D == 128 || D == 256;
+}
+
+const char* score_mfma_name(int layout, int bits, int C, int B, int D) {
+    if (!score_mfma_supported(layout, bits, C, B, D)) return nullptr;
+    const int mt = mt_for(B, D);
+    if (layout == 0) return mt == 4 ? "mfma32_unpacked_mt4" : mt == 2 ? "mfma32_unpacked_mt2" : "mfma32_unpacked_mt1";
+    if (bits == 2) return mt == 4 ? "mfma32_packed2_mt4" : mt == 2 ? "mfma32_packed2_mt2" : "mfma32_packed2_mt1";
+    return mt == 4 ? "mfma32_packed3_mt4" : mt == 2 ? "mfma32_packed3_mt2" : "mfma32_packed3_mt1";
+}
+
+hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
+                             int layout, int bits, const float* codebook, int C,
+                             float* scores, int P, int B, int S, int D,
+                             hipStream_t stream) {
+    if (layout == 0) return launch_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+    if (bits == 2) return launch_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+    return launch_layout<1, 3>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+}
+
+}  // namespace tq

@@ -1,0 +1,50 @@
+// Shared host/device definitions for the compressed-key scoring kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// sqrt(pi/2): the QJL de-biasing constant; the estimator divides it by the
+// number of projection rows, D ("TurboQuant: Rotate-then-Quantize KV Caches at
+// 3 Bits", section 3, the QJL bullet).
+constexpr double kSqrtHalfPi = 1.2533141373155002512078826424055;
+
+struct KeyStreams {
+    const uint8_t* idx;    // unpacked: [P,S,D] bytes; packed: [P,S,D*bits/8]
+    const uint8_t* sign;   // unpacked: [P,S,D] int8 +-1; packed: [P,S,D/8] bits
+    const void* gamma;     // unpacked: float [P,S]; packed: _Float16 [P,S]
+};
+
+// Bytes of one key's index stream, sign stream and gamma for a layout.
+__host__ __device__ inline int64_t idx_row_bytes(int layout, int bits, int D) {
+    return layout == 0 ? (int64_t)D : (int64_t)D * bits / 8;
+}
+__host__ __device__ inline int64_t sign_row_bytes(int layout, int D) {
+    return layout == 0 ? (int64_t)D : (int64_t)D / 8;
+}
+
+// Kernel launchers (defined in the .hip files; all return hipError_t of the launch).
+hipError_t launch_query_transform(const float* q, const float* Pi, const float* S_mat,
+                                  float* A, float* T, int P, int H, int B, int D,
+                                  hipStream_t stream);
+
+hipError_t launch_score_valu(const float* A, const float* T, KeyStreams keys,
+                             int layout, int bits, const float* codebook, int C,
+                             float* scores, int P, int B, int S, int D,
+                             hipStream_t stream);
+
+// Returns false if the MFMA kernels do not cover (layout, bits, C, B, D).
+bool score_mfma_supported(int layout, int bits, int C, int B, int D);
+const char* score_mfma_name(int layout, int bits, int C, int B, int D);
+hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
+                             int layout, int bits, const float* codebook, int C,
+                             float* scores, int P, int B, int S, int D,
+                             hipStream_t stream);
+
+hipError_t launch_decode(KeyStreams keys, int layout, int bits,
+                         uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
+                         int P, int S, int D, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,167 @@
+/*
+ * tq.h -- C ABI of the compressed-key attention scoring library (MI355X, gfx950).
+ *
+ * The library scores queries against a TurboQuant-compressed key cache without
+ * rebuilding any key. A compressed key s holds, per coordinate d, a codebook
+ * index idx[s,d] and a QJL sign sigma[s,d] in {-1,+1}, plus one residual norm
+ * gamma[s]. Its raw score against query q_b is
+ *
+ *   scores[b,s] = sum_d A[b,d] * codebook[idx[s,d]]
+ *               + (sqrt(pi/2) / D) * gamma[s] * sum_d T[b,d] * sigma[s,d]
+ *
+ * with A = Pi q_b and T = S_mat q_b computed once per query. No softmax, no
+ * 1/sqrt(D) scaling, no values. Source: "TurboQuant Attention in CUDA:
+ * Transform the Query, Reuse the Work" (riteshyadav.xyz), sections "Move the
+ * transforms to the query" and "Two kernels, two jobs"; the reconstruction
+ * this equals is the inner-product quantizer of "TurboQuant: Rotate-then-
+ * Quantize KV Caches at 3 Bits" (kanthi.in), section 3.
+ *
+ * Conventions for every entry point
+ *  - All array arguments are DEVICE pointers (memory of the current HIP
+ *    device), row-major, densely packed, with base addresses aligned to
+ *    16 bytes. The caller allocates and owns every buffer; the library
+ *    allocates nothing and keeps no state between calls, so calls are
+ *    reentrant. Outputs must not alias inputs.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously; results are visible after the stream
+ *    synchronizes. Calls on one stream run in order.
+ *  - Arguments are validated on the host before anything is launched. The
+ *    return value is TQ_OK or a negative TQ_ERR_* code; nothing is thrown
+ *    across the ABI. TQ_ERR_LAUNCH reports a HIP error from the launch.
+ *  - Empty calls: if P, B or S is 0 (after the format checks pass) nothing is
+ *    launched, TQ_OK is returned, and array pointers may be NULL. Negative
+ *    sizes, and D <= 0 or H <= 0, are TQ_ERR_ARG.
+ *  - Problems: P independent scoring problems are handled in one call. With H
+ *    heads, problem p uses head p % H (its own Pi and S_mat); P % H must be 0.
+ *  - Not checked (as in the page's challenge, where indices are guaranteed
+ *    valid): unpacked indices must be < C and unpacked signs must be +-1.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TQ_OK               0
+#define TQ_ERR_ARG         -1  /* null pointer, negative size, D or H <= 0, P % H != 0, unknown layout/kernel */
+#define TQ_ERR_UNSUPPORTED -2  /* shape or format outside what the kernels support (see tq_score) */
+#define TQ_ERR_ALIGN       -3  /* a base pointer is not 16-byte aligned */
+#define TQ_ERR_LAUNCH      -4  /* HIP reported an error launching a kernel */
+
+/* key layouts */
+#define TQ_UNPACKED 0
+#define TQ_PACKED   1
+
+/* largest supported coordinate count D */
+#define TQ_MAX_D 1024
+
+/*
+ * Compressed keys of P problems, S keys each, D coordinates per key.
+ *
+ * layout == TQ_UNPACKED ("TurboQuant Attention in CUDA", section "Full CUDA
+ * solution": one byte per index and per sign):
+ *   idx   uint8  [P, S, D]   codebook index, < C
+ *   sign  int8   [P, S, D]   +1 or -1
+ *   gamma float32 [P, S]     residual norm
+ *   bits  ignored
+ *
+ * layout == TQ_PACKED (bitstreams, one run of bytes per key):
+ *   idx   uint8 [P, S, D*bits/8]  coordinate d occupies bits [bits*d, bits*d+bits)
+ *                                 of the key's bytes read as one little-endian
+ *                                 integer (LSB-first, as the 2-bit extraction of
+ *                                 "Fitting 4.4x More Context on Jetson", section
+ *                                 "v6: Fused Vectorized Hybrid"; a 128-dim 3-bit
+ *                                 key is 48 bytes, "TurboQuant: Rotate-then-
+ *                                 Quantize", section 8)
+ *   sign  uint8 [P, S, D/8]       bit d (LSB-first) is 1 for sigma = +1, 0 for -1
+ *   gamma float16 [P, S]          residual norm as IEEE binary16
+ *   bits  2 or 3; C must equal 2^bits; D must be a multiple of 8
+ */
+typedef struct tq_keys {
+    int32_t layout;
+    int32_t bits;
+    const void* idx;
+    const void* sign;
+    const void* gamma;
+} tq_keys;
+
+/*
+ * tq_query_transform: A = Pi q and T = S_mat q for every query.
+ * "TurboQuant Attention in CUDA", section "Move the transforms to the query";
+ * indexing as the comment over its first kernel: A[b,d] = sum_j Pi[d,j] q[b,j].
+ *
+ *   q      float32 [P, B, D]   queries
+ *   Pi     float32 [H, D, D]   rotation of each head, row-major
+ *   S_mat  float32 [H, D, D]   QJL projection of each head, row-major
+ *   A, T   float32 [P, B, D]   outputs (problem p uses head p % H)
+ *
+ * Arithmetic is fp32 with fp32 accumulation. D <= TQ_MAX_D.
+ */
+int tq_query_transform(const float* q, const float* Pi, const float* S_mat,
+                       float* A, float* T,
+                       int P, int H, int B, int D, void* stream);
+
+/*
+ * tq_score: raw scores of B transformed queries against S compressed keys,
+ * for each of P problems (formula at the top of this file; "TurboQuant
+ * Attention in CUDA", sections "Two kernels, two jobs" and "Full CUDA
+ * solution", with the packed layouts above added).
+ *
+ *   A, T      float32 [P, B, D]   from tq_query_transform
+ *   keys      compressed keys (struct above; host pointer to the struct,
+ *             device pointers inside it)
+ *   codebook  float32 [C]         centroids (C <= 256 unpacked, 2^bits packed)
+ *   scores    float32 [P, B, S]   output
+ *
+ * Result: fp32, within 1e-4 * (1 + |exact|) of the exact (float64) value of
+ * the formula for the given inputs. D <= TQ_MAX_D, B <= 262144, P <= 65535.
+ */
+int tq_score(const float* A, const float* T, const tq_keys* keys,
+             const float* codebook, int C, float* scores,
+             int P, int B, int S, int D, void* stream);
+
+/* kernel families tq_score can use; TQ_KERNEL_AUTO picks by shape */
+#define TQ_KERNEL_AUTO   0
+#define TQ_KERNEL_VALU   1  /* any shape: one key per lane, fp32 FMAs */
+#define TQ_KERNEL_MFMA   2  /* C <= 8 and D in {64, 128, 256} (also 32 when unpacked):
+                               split-f16 matrix-core contraction */
+
+/*
+ * tq_score_with_kernel: tq_score with an explicit kernel family, so that every
+ * family can be checked on every shape it supports. TQ_ERR_UNSUPPORTED if the
+ * family cannot run the shape. tq_score == tq_score_with_kernel(..., AUTO).
+ */
+int tq_score_with_kernel(const float* A, const float* T, const tq_keys* keys,
+                         const float* codebook, int C, float* scores,
+                         int P, int B, int S, int D, int kernel, void* stream);
+
+/*
+ * tq_score_kernel_name: name of the kernel tq_score_with_kernel would launch
+ * for this shape and format, or NULL if unsupported. Host-only, no GPU work.
+ */
+const char* tq_score_kernel_name(int layout, int bits, int C, int B, int D, int kernel);
+
+/*
+ * tq_decode_debug: expand keys of either layout into the unpacked layout,
+ * bit-exactly (gamma is widened to float32, which is exact from fp16).
+ *
+ *   keys       compressed keys (struct above)
+ *   idx_out    uint8  [P, S, D]
+ *   sign_out   int8   [P, S, D]   +-1
+ *   gamma_out  float32 [P, S]
+ */
+int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out,
+                    float* gamma_out, int P, int S, int D, void* stream);
+
+/* tq_status_string: static description of a status code. */
+const char* tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -45,9 +45,14 @@ class Workload:
     def score_bytes(self) -> int:
         return self.P * self.B * self.S * 4
 
+    def query_bytes(self) -> int:
+        """Transformed queries A and T (fp32) and the fp32 codebook the score pass reads."""
+        return 2 * self.P * self.B * self.D * 4 + self.C * 4
+
     def algorithmic_bytes(self) -> int:
-        """Bytes the score pass must move: compressed keys in, fp32 scores out."""
-        return self.key_bytes() + self.score_bytes()
+        """Bytes the score pass must move once: compressed keys, A, T and the
+        codebook in, fp32 scores out."""
+        return self.key_bytes() + self.query_bytes() + self.score_bytes()
 
     def algorithmic_flops(self) -> int:
         """4D + 3 flops per (query, key) pair: two D-long dots and the combine."""

@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/tq.h
+declares, and rejects bad arguments with the documented codes before anything
+reaches a GPU (no compute call is made here)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+import compressed_attention_scoring_amd as tq
+
+EXPECTED = {
+    "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
+    "tq_decode_debug", "tq_status_string",
+}
+OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
+
+
+def test_header_declares_expected_functions():
+    assert set(tq.header_functions()) == EXPECTED
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(tq.library_path())
+    for name in tq.header_functions():
+        assert getattr(lib, name) is not None
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert EXPECTED <= exported
+
+
+def test_status_strings():
+    assert tq.tq_status_string(0) == "ok"
+    for code in (ARG, UNSUP, ALIGN, -4):
+        assert tq.tq_status_string(code) not in ("ok", "unknown status")
+    assert tq.tq_status_string(-99) == "unknown status"
+
+
+def test_kernel_names_host_only():
+    assert tq.tq_score_kernel_name("unpacked", 0, 4, 32, 128) == "mfma32_unpacked_mt1"
+    assert tq.tq_score_kernel_name("packed", 2, 4, 32, 128) == "mfma32_packed2_mt1"
+    assert tq.tq_score_kernel_name("packed", 3, 8, 4, 128) == "mfma32_packed3_mt1"
+    assert tq.tq_score_kernel_name("packed", 3, 8, 128, 128) == "mfma32_packed3_mt4"
+    assert tq.tq_score_kernel_name("unpacked", 0, 4, 1, 2) == "valu_unpacked"
+    assert tq.tq_score_kernel_name("unpacked", 0, 16, 32, 128) == "valu_unpacked"
+    assert tq.tq_score_kernel_name("unpacked", 0, 4, 32, 128, "valu") == "valu_unpacked"
+    assert tq.tq_score_kernel_name("packed", 2, 4, 32, 48, "mfma") is None
+    assert tq.tq_score_kernel_name("packed", 2, 8, 32, 128) is None      # C != 2^bits
+    assert tq.tq_score_kernel_name("packed", 4, 16, 32, 128) is None     # 4-bit not supported
+
+
+def _keys(layout=0, bits=0, idx=16, sign=16, gamma=16):
+    return tq._CKeys(layout, bits, idx, sign, gamma)
+
+
+def _score(keys, C=4, P=1, B=2, S=8, D=32, A=16, T=16, cb=16, out=16, kernel=0):
+    return tq._lib.tq_score_with_kernel(A, T, ctypes.byref(keys), cb, C, out, P, B, S, D, kernel, None)
+
+
+def test_score_rejects_bad_arguments_before_launch():
+    # pointers are never dereferenced on these paths; 16 is a stand-in aligned address
+    assert _score(_keys(idx=None)) == ARG
+    assert _score(_keys(), A=None) == ARG
+    assert tq._lib.tq_score_with_kernel(16, 16, None, 16, 4, 16, 1, 2, 8, 32, 0, None) == ARG
+    assert _score(_keys(layout=5)) == ARG
+    assert _score(_keys(), S=-1) == ARG
+    assert _score(_keys(), D=0) == ARG
+    assert _score(_keys(), kernel=7) == ARG
+    assert _score(_keys(layout=1, bits=4), C=16) == UNSUP
+    assert _score(_keys(layout=1, bits=2), C=8) == UNSUP
+    assert _score(_keys(layout=1, bits=3), C=8, D=12) == UNSUP
+    assert _score(_keys(), C=300) == UNSUP
+    assert _score(_keys(), D=2048) == UNSUP
+    assert _score(_keys(), P=70000) == UNSUP
+    assert _score(_keys(), B=300000) == UNSUP
+    assert _score(_keys(layout=1, bits=2), C=4, D=48, kernel=2) == UNSUP   # MFMA needs D in {64,128,256}
+    assert _score(_keys(idx=17)) == ALIGN
+    assert _score(_keys(gamma=18)) == ALIGN
+
+
+def test_empty_calls_are_no_ops():
+    assert _score(_keys(idx=None, sign=None, gamma=None), S=0, A=None, T=None, cb=None, out=None) == OK
+    assert _score(_keys(), B=0) == OK
+    assert _score(_keys(), P=0) == OK
+    assert tq._lib.tq_query_transform(None, None, None, None, None, 0, 1, 4, 8, None) == OK
+    assert tq._lib.tq_decode_debug(ctypes.byref(_keys()), None, None, None, 1, 0, 8, None) == OK
+
+
+def test_query_transform_rejects_bad_arguments():
+    f = tq._lib.tq_query_transform
+    assert f(16, 16, 16, 16, None, 1, 1, 2, 8, None) == ARG
+    assert f(16, 16, 16, 16, 16, 3, 2, 2, 8, None) == ARG        # P % H != 0
+    assert f(16, 16, 16, 16, 16, 1, 0, 2, 8, None) == ARG
+    assert f(16, 16, 16, 16, 16, 1, 1, 2, 0, None) == ARG
+    assert f(16, 16, 16, 16, 16, 1, 1, 2, 2000, None) == UNSUP
+    assert f(20, 16, 16, 16, 16, 1, 1, 2, 8, None) == ALIGN
+
+
+def test_decode_rejects_bad_arguments():
+    f = tq._lib.tq_decode_debug
+    assert f(ctypes.byref(_keys()), None, 16, 16, 1, 4, 8, None) == ARG
+    assert f(ctypes.byref(_keys(layout=1, bits=5)), 16, 16, 16, 1, 4, 8, None) == UNSUP
+    assert f(ctypes.byref(_keys(sign=33)), 16, 16, 16, 1, 4, 8, None) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(2, 8)
+    Pi = torch.eye(8)
+    with pytest.raises(ValueError, match="GPU"):
+        tq.tq_query_transform(q, Pi, Pi)

@@ -36,7 +36,7 @@ def test_unit_keys_and_outliers():
 def test_workload_table():
     w = synth.workload("decode")
     assert (w.B, w.S, w.D, w.C, w.layout) == (32, 32768, 128, 4, "unpacked")
-    assert w.algorithmic_bytes() == 32768 * 260 + 32 * 32768 * 4
+    assert w.algorithmic_bytes() == 32768 * 260 + 32 * 32768 * 4 + 2 * 32 * 128 * 4 + 4 * 4
     g = synth.workload("gqa")
     assert g.P == 128 and g.H == 8 and g.B == 4 and g.key_bytes() == 128 * 32768 * 66
 
