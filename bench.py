@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode",
                     help="decode (default, the quoted configuration); others for profiling")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "valu", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -211,7 +212,7 @@ def main() -> int:
         raise SystemExit("bench.py needs a GPU")
     device = torch.device("cuda:0")
     w = synth.workload(args.workload)
-    kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.B, w.D, args.kernel)
+    kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, args.kernel)
     log(f"workload {w.describe()} kernel {kname}")
     ring, shared, host, per_set = build_ring(w, device, w.seed)
     log(f"ring of {len(ring)} buffer sets, {len(ring) * per_set / 1e6:.0f} MB")

@@ -8,7 +8,7 @@ functions keep the C names:
     tq_score(A, T, keys, codebook)             -> scores
     tq_score_with_kernel(A, T, keys, codebook, kernel)
     tq_decode_debug(keys, D)                   -> (idx, sign, gamma)
-    tq_score_kernel_name(layout, bits, C, B, D, kernel)
+    tq_score_kernel_name(layout, bits, C, P, B, S, D, kernel)
 
 Only argument marshalling happens here: shapes, dtypes, contiguity and device
 are checked, output tensors are allocated with torch, and pointers plus the
@@ -66,7 +66,7 @@ def _load():
     lib.tq_score_with_kernel.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, vp,
                                          i32, i32, i32, i32, i32, vp]
     lib.tq_score_with_kernel.restype = i32
-    lib.tq_score_kernel_name.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.tq_score_kernel_name.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     lib.tq_score_kernel_name.restype = ctypes.c_char_p
     lib.tq_decode_debug.argtypes = [ctypes.POINTER(_CKeys), vp, vp, vp, i32, i32, i32, vp]
     lib.tq_decode_debug.restype = i32
@@ -230,9 +230,11 @@ def tq_score(A, T, keys: Keys, codebook, scores=None, stream=None):
     return tq_score_with_kernel(A, T, keys, codebook, "auto", scores, stream)
 
 
-def tq_score_kernel_name(layout: str, bits: int, C: int, B: int, D: int, kernel: str = "auto"):
+def tq_score_kernel_name(layout: str, bits: int, C: int, P: int, B: int, S: int, D: int,
+                         kernel: str = "auto"):
+    """Name of the kernel tq_score would launch for this shape, or None if unsupported."""
     lay = TQ_UNPACKED if layout == "unpacked" else TQ_PACKED
-    name = _lib.tq_score_kernel_name(lay, int(bits), int(C), int(B), int(D), KERNELS[kernel])
+    name = _lib.tq_score_kernel_name(lay, int(bits), int(C), int(P), int(B), int(S), int(D), KERNELS[kernel])
     return None if name is None else name.decode()
 
 

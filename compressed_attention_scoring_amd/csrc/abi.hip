@@ -87,16 +87,16 @@ int tq_query_transform(const float* q, const float* Pi, const float* S_mat, floa
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
-const char* tq_score_kernel_name(int layout, int bits, int C, int B, int D, int kernel) {
+const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int S, int D, int kernel) {
     if (layout != TQ_UNPACKED && layout != TQ_PACKED) return nullptr;
-    if (B <= 0 || D <= 0 || D > TQ_MAX_D) return nullptr;
+    if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D) return nullptr;
     if (layout == TQ_PACKED && ((bits != 2 && bits != 3) || D % 8 || C != (1 << bits))) return nullptr;
     if (layout == TQ_UNPACKED && (C < 1 || C > 256)) return nullptr;
+    const int b = layout == TQ_PACKED ? bits : 0;
     if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(layout, bits, C, B, D);
-    if (kernel == TQ_KERNEL_MFMA)
-        return tq::score_mfma_name(layout, layout == TQ_PACKED ? bits : 0, C, B, D);
     if (kernel == TQ_KERNEL_VALU)
         return layout == TQ_UNPACKED ? "valu_unpacked" : bits == 2 ? "valu_packed2" : "valu_packed3";
+    if (kernel == TQ_KERNEL_MFMA) return tq::score_mfma_name(layout, b, C, B, D);
     return nullptr;
 }
 

@@ -8,12 +8,13 @@
 // W_h = [Pi_h ; S_mat_h] (2D x D) produce [A | T] in one fp32 product
 // Y[p, b, r] = sum_j W_h[r, j] q[p, b, j], r < 2D.
 //
-// The product is tiny (4 P B D^2 flops) and latency-bound, so the kernel is
-// shaped for few dependent memory rounds: a 256-lane workgroup owns 16 rows of
-// W and 32 queries of one problem; for D <= 256 all of its operands (16 W rows
-// and the 32 query rows) are requested in a single round of 16-byte loads into
-// LDS, then every lane forms two outputs from broadcast LDS reads with eight
-// independent fp32 FMA chains. Larger D is staged in 256-column chunks.
+// The product is tiny (4 P B D^2 flops) and latency-bound, so both variants are
+// shaped for few dependent memory rounds. D a multiple of 32 up to 256 runs on
+// the matrix cores (query_transform_mfma_kernel below). Other D use the vector
+// kernel: a 256-lane workgroup owns 16 rows of W and 32 queries of one problem;
+// its operands are requested in one round of loads into LDS per 256 columns,
+// then every lane forms two outputs from broadcast LDS reads with eight
+// independent fp32 FMA chains.
 #include "tq_common.hpp"
 
 namespace tq {
@@ -119,11 +120,94 @@ __global__ __launch_bounds__(256) void query_transform_kernel(
     if (b0 + bq + 16 < B) out[((int64_t)p * B + b0 + bq + 16) * D + d] = y1;
 }
 
+// Matrix-core variant for D in {32, 64, ..., 256} (D % 32 == 0): one 32x32 tile
+// of Y (32 queries x 32 rows of W) per workgroup, contracted with fp32 MFMA
+// (v_mfma_f32_32x32x2_f32: fp32 operands, fp32 accumulation, so no operand
+// splitting is needed). The contraction over D is split across the 4 wavefronts
+// (D/4 coordinates each, D/8 per lane half); every lane loads its operands for
+// the whole contraction with 16-byte loads in one round, and the four partial
+// tiles are summed through LDS. Queries are the MFMA rows and W rows the
+// columns, so the output rows of A and T are written as contiguous 128-byte runs.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int D>
+__global__ __launch_bounds__(256) void query_transform_mfma_kernel(
+    const float* __restrict__ q, const float* __restrict__ Pi,
+    const float* __restrict__ S_mat, float* __restrict__ A, float* __restrict__ T,
+    int H, int B) {
+    constexpr int KL = D / 8;                     // coordinates per lane half per wavefront
+    __shared__ float part[4][64][17];             // partial tiles, padded against bank conflicts
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * 32;               // first row of W = [Pi; S_mat] (2D rows)
+    const int b0 = blockIdx.y * 32;
+    const int p = blockIdx.z;
+    const int h = p % H;
+    const int i = lane & 31, half = lane >> 5;
+    const int k0 = wave * (D / 4) + half * KL;
+
+    const int wr = r0 + i;                        // W row this lane feeds (always < 2D)
+    const float* wsrc = wr < D ? Pi + ((int64_t)h * D + wr) * D : S_mat + ((int64_t)h * D + wr - D) * D;
+    const int b = b0 + i;
+    const int bc = b < B ? b : B - 1;             // unconditional load; zeroed below when b >= B
+    const float* qsrc = q + ((int64_t)p * B + bc) * D;
+    float wv[KL], qv[KL];
+#pragma unroll
+    for (int k = 0; k < KL; k += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(wsrc + k0 + k);
+        const float4 y = *reinterpret_cast<const float4*>(qsrc + k0 + k);
+        wv[k] = x.x; wv[k + 1] = x.y; wv[k + 2] = x.z; wv[k + 3] = x.w;
+        qv[k] = y.x; qv[k + 1] = y.y; qv[k + 2] = y.z; qv[k + 3] = y.w;
+    }
+    if (b >= B) {
+#pragma unroll
+        for (int k = 0; k < KL; ++k) qv[k] = 0.f;
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[k], wv[k], acc, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[wave][lane][v] = acc[v];
+    __syncthreads();
+
+    // thread -> (lane of the tile layout, 4 of its 16 accumulator slots)
+    const int l = tid & 63, vg = tid >> 6;
+    const int col = l & 31;
+    const int row_base = 4 * (l >> 5);
+    const int wcol = r0 + col;
+    float* out = wcol < D ? A : T;
+    const int d = wcol < D ? wcol : wcol - D;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int v = 4 * vg + u;
+        const float y = (part[0][l][v] + part[1][l][v]) + (part[2][l][v] + part[3][l][v]);
+        const int row = 8 * (v >> 2) + row_base + (v & 3);
+        const int bb = b0 + row;
+        if (bb < B) out[((int64_t)p * B + bb) * D + d] = y;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_query_transform(const float* q, const float* Pi, const float* S_mat,
                                   float* A, float* T, int P, int H, int B, int D,
                                   hipStream_t stream) {
+    if (D % 32 == 0 && D <= 256) {
+        dim3 grid(2 * D / 32, (B + 31) / 32, P);
+        switch (D) {
+            case 32: hipLaunchKernelGGL(query_transform_mfma_kernel<32>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 64: hipLaunchKernelGGL(query_transform_mfma_kernel<64>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 96: hipLaunchKernelGGL(query_transform_mfma_kernel<96>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 128: hipLaunchKernelGGL(query_transform_mfma_kernel<128>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 160: hipLaunchKernelGGL(query_transform_mfma_kernel<160>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 192: hipLaunchKernelGGL(query_transform_mfma_kernel<192>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 224: hipLaunchKernelGGL(query_transform_mfma_kernel<224>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            default: hipLaunchKernelGGL(query_transform_mfma_kernel<256>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+        }
+        return hipGetLastError();
+    }
     const int kc = D < kChunk ? D : kChunk;
     const size_t lds = (size_t)(kRows + kQueries) * (((kc + 3) & ~3) + kPad) * sizeof(float);
     dim3 grid((2 * D + kRows - 1) / kRows, (B + kQueries - 1) / kQueries, P);

@@ -336,9 +336,10 @@ __device__ __forceinline__ void load_dwords(const uint8_t* __restrict__ p, uint3
     for (; i < N; ++i) v[i] = q[i];
 }
 
-constexpr int align_of_half(int row_bytes) {
-    // lane halves start at key * row + (0 or row / 2) from a 16-byte aligned base
-    return (row_bytes / 2) % 16 == 0 ? 16 : (row_bytes / 2) % 8 == 0 ? 8 : 4;
+constexpr int align_of_seg(int row_bytes, int seg_bytes) {
+    // a lane's segment starts at key * row + m * seg from a 16-byte aligned base
+    return (row_bytes % 16 == 0 && seg_bytes % 16 == 0) ? 16
+         : (row_bytes % 8 == 0 && seg_bytes % 8 == 0) ? 8 : 4;
 }
 
 __device__ __forceinline__ float pow2_scale_for(float maxabs) {
@@ -356,8 +357,8 @@ __device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
     lo = __builtin_bit_cast(uint16_t, l);
 }
 
-// One 32-key tile's compressed codes for this lane: its key's half of the index
-// and sign streams, and the key's gamma.
+// One 32-key tile's compressed codes for this lane: its segment of the key's
+// index and sign streams, and the key's gamma.
 template <int NI, int NS>
 struct TileCodes {
     uint32_t iw[NI];
@@ -365,18 +366,21 @@ struct TileCodes {
     float gam;
 };
 
+// Segment m (0 or 1) of a key: coordinates [m*D/2, (m+1)*D/2).
 template <int LAYOUT, int BITS, int D>
 __device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
                                                     Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
                                           const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
-                                          const void* __restrict__ gamma, int64_t key, int g) {
+                                          const void* __restrict__ gamma, int64_t key, int m) {
     using F = Fmt<LAYOUT, BITS>;
     constexpr int NI = F::template idx_dw<D>();
     constexpr int NS = F::template sign_dw<D>();
     constexpr int IDX_ROW = F::template idx_row<D>();
     constexpr int SIGN_ROW = F::template sign_row<D>();
-    load_dwords<NI, align_of_half(IDX_ROW)>(idx + key * IDX_ROW + g * (IDX_ROW / 2), c.iw);
-    load_dwords<NS, align_of_half(SIGN_ROW)>(sign + key * SIGN_ROW + g * (SIGN_ROW / 2), c.sw);
+    constexpr int IDX_SEG = IDX_ROW / 2;
+    constexpr int SIGN_SEG = SIGN_ROW / 2;
+    load_dwords<NI, align_of_seg(IDX_ROW, IDX_SEG)>(idx + key * IDX_ROW + m * IDX_SEG, c.iw);
+    load_dwords<NS, align_of_seg(SIGN_ROW, SIGN_SEG)>(sign + key * SIGN_ROW + m * SIGN_SEG, c.sw);
     if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
     else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
 }
@@ -388,8 +392,8 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
     float* __restrict__ scores, int B, int S, float coef) {
     using F = Fmt<LAYOUT, BITS>;
+    constexpr int HALF = D / 2;                // coordinates per lane segment
     constexpr int KS = D / 16;                 // k-steps (16 coordinates each)
-    constexpr int HALF = D / 2;                // coordinates per lane half
     constexpr int NI = F::template idx_dw<D>();
     constexpr int NS = F::template sign_dw<D>();
     constexpr int BLOCK = 64 * 16;             // one operand block: 64 lanes x 16 bytes
@@ -397,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     constexpr int SEG = 16;                    // coordinates each prologue lane converts
     constexpr int PER_ROW = D / SEG;           // prologue lanes per query row
     constexpr int ROWS_PER_PASS = kThreads / PER_ROW;
+    static_assert(HALF % SEG == 0, "the prologue converts 16-coordinate blocks inside one lane segment");
 
     __shared__ __attribute__((aligned(16))) uint8_t ops[OPS_BYTES];
     __shared__ float2 rowk[MT * 32];           // per-row epilogue factors (M, R)
@@ -410,58 +415,70 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     const int col = lane & 31;
     const int g = lane >> 5;
     const int ntiles = (S + kTileKeys - 1) / kTileKeys;
-    const int stride = gridDim.x * kWaves;
     const int64_t key0 = (int64_t)p * S;
 
-    // ---- the first tile's codes are requested before anything else, so the
-    //      HBM latency overlaps building the query-side operands
     int tile = blockIdx.x * kWaves + wave;
+    const int stride = gridDim.x * kWaves;
     TileCodes<NI, NS> cur;
-    if (tile < ntiles) {
-        const int s = min(tile * kTileKeys + col, S - 1);
-        load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
-    }
 
-    // ---- codebook: power-of-two scale, f16 hi/lo split, byte tables for v_perm
-    float cbv[8];
-    float mc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        cbv[k] = k < C ? codebook[k] : 0.f;
-        mc = fmaxf(mc, fabsf(cbv[k]));
-    }
-    const float sc = pow2_scale_for(mc);
+    // codebook byte tables for v_perm lookups and its scale, filled in the
+    // prologue once A, T and the first tile's codes have been requested
+    float sc = 1.f;
     uint32_t tab_hi[4] = {0u, 0u, 0u, 0u}, tab_lo[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint16_t hb, lb;
-        split_f16(cbv[k] * sc, hb, lb);
-        const int w = k >> 2, sh = 8 * (k & 3);
-        tab_hi[w] |= (uint32_t)(hb & 0xffu) << sh;
-        tab_hi[2 + w] |= (uint32_t)(hb >> 8) << sh;
-        tab_lo[w] |= (uint32_t)(lb & 0xffu) << sh;
-        tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
-    }
 
     // ---- query-side operands: each row of A and T is scaled by its own power of
-    //      two (row max found by the 8 lanes that hold the row), split into f16
+    //      two (row max found by the lanes that hold the row), split into f16
     //      hi/lo and stored at the slot its coordinate occupies in the operands
     const float* Ap = A + ((int64_t)p * B + b0) * D;
     const float* Tp = T + ((int64_t)p * B + b0) * D;
     for (int r0 = 0; r0 < MT * 32; r0 += ROWS_PER_PASS) {
         const int row = r0 + tid / PER_ROW;            // row within this workgroup's tiles
-        const int part = tid % PER_ROW;                // coordinates 16*part .. 16*part+15
+        const int pl = tid % PER_ROW;                  // coordinates 16*pl .. 16*pl+15
         float a[SEG], t[SEG];
         float ma = 0.f, mt = 0.f;
-        if (row < rows) {
+        // Loads are unconditional (rows past the end re-read the last row and are
+        // zeroed below) so that the compiler's wait counts stay exact.
+        const int rowc = min(row, rows - 1);
 #pragma unroll
-            for (int k = 0; k < SEG; k += 4) {
-                const float4 va = *reinterpret_cast<const float4*>(Ap + (int64_t)row * D + part * SEG + k);
-                const float4 vt = *reinterpret_cast<const float4*>(Tp + (int64_t)row * D + part * SEG + k);
-                a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
-                t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+        for (int k = 0; k < SEG; k += 4) {
+            const float4 va = *reinterpret_cast<const float4*>(Ap + (int64_t)rowc * D + pl * SEG + k);
+            const float4 vt = *reinterpret_cast<const float4*>(Tp + (int64_t)rowc * D + pl * SEG + k);
+            a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
+            t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+        }
+        // The first tile's codes are requested right behind the first rows of A
+        // and T: vector loads retire in issue order, so converting A and T waits
+        // only for them while the key bytes are still in flight from HBM. An empty
+        // asm with a memory clobber keeps the compiler from moving the key loads
+        // above the A and T loads (it emits no instruction); the key load is
+        // unconditional too (a wave without a tile re-reads a valid key).
+        if (r0 == 0) {
+            asm volatile("" ::: "memory");
+            const int s = min(min(tile, ntiles - 1) * kTileKeys + col, S - 1);
+            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
+            asm volatile("" ::: "memory");
+            // codebook: power-of-two scale, f16 hi/lo split, byte tables. Its loads
+            // come after the vector loads above so their latency is not paid first.
+            float cbv[8];
+            float mc = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                cbv[k] = k < C ? codebook[k] : 0.f;
+                mc = fmaxf(mc, fabsf(cbv[k]));
             }
-        } else {
+            sc = pow2_scale_for(mc);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                uint16_t hb, lb;
+                split_f16(cbv[k] * sc, hb, lb);
+                const int w = k >> 2, sh = 8 * (k & 3);
+                tab_hi[w] |= (uint32_t)(hb & 0xffu) << sh;
+                tab_hi[2 + w] |= (uint32_t)(hb >> 8) << sh;
+                tab_lo[w] |= (uint32_t)(lb & 0xffu) << sh;
+                tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
+            }
+        }
+        if (row >= rows) {
 #pragma unroll
             for (int k = 0; k < SEG; ++k) a[k] = t[k] = 0.f;
         }
@@ -477,11 +494,13 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         }
         const float sA = pow2_scale_for(ma);
         const float sT = pow2_scale_for(mt);
-        if (row < MT * 32 && part == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
+        // sA, sT and sc are powers of two, so these factors are exact
+        if (row < MT * 32 && pl == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
         if (row < MT * 32) {
             const int mtile = row / 32, rl = row % 32;
-            const int gg = (part * SEG) / HALF;                 // lane half holding these coordinates
-            const int blk16 = ((part * SEG) % HALF) / SEG;      // their 16-coordinate block in the half
+            const int d0 = pl * SEG;
+            const int gg = d0 / HALF;                           // lane segment holding these coordinates
+            const int blk16 = (d0 % HALF) / SEG;                // their 16-coordinate block in it
             uint8_t* lane_base = ops + (mtile * KS * 4) * BLOCK + (gg * 32 + rl) * 16;
 #pragma unroll
             for (int k = 0; k < SEG; ++k) {
@@ -503,12 +522,14 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     __syncthreads();
 
     float* out_p = scores + ((int64_t)p * B + b0) * S;
+    const uint8_t* my_ops = ops + lane * 16;
 
     while (tile < ntiles) {
         const int next = tile + stride;
         TileCodes<NI, NS> nxt;
-        if (next < ntiles) {   // prefetch the next tile while this one is computed
-            const int s = min(next * kTileKeys + col, S - 1);
+        {   // prefetch the next tile while this one is computed (clamped and
+            // unconditional, like the first load)
+            const int s = min(min(next, ntiles - 1) * kTileKeys + col, S - 1);
             load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma, key0 + s, g);
         }
 
@@ -531,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             F::template signs<NS>(cur.sw, j, sg.u);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* base = ops + ((mt * KS + j) * 4) * BLOCK + lane * 16;
+                const uint8_t* base = my_ops + ((mt * KS + j) * 4) * BLOCK;
                 Op8 ahi, alo, thi, tlo;
                 *reinterpret_cast<uint4*>(ahi.u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
                 *reinterpret_cast<uint4*>(alo.u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
@@ -556,7 +577,9 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
                     const int row = mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
                     if (row < rows) {
                         const float2 k = rowk[row];
-                        out_p[(int64_t)row * S + s] = fmaf(k.y * cur.gam, accR[mt][v], accM[mt][v] * k.x);
+                        // scores are written once and not read again here: stream them past the caches
+                        __builtin_nontemporal_store(fmaf(k.y * cur.gam, accR[mt][v], accM[mt][v] * k.x),
+                                                    out_p + (int64_t)row * S + s);
                     }
                 }
             }
@@ -586,20 +609,20 @@ int mt_for(int B, int D) {
 template <int LAYOUT, int BITS, int D, int MT>
 hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                      float* scores, int P, int B, int S, hipStream_t stream) {
-    const int groups = (B + MT * 32 - 1) / (MT * 32);
+    const int groups_y = (B + MT * 32 - 1) / (MT * 32);
     const int ntiles = (S + kTileKeys - 1) / kTileKeys;
-    const int per_tile = (D / 16) * 4 * 1024 * MT;
-    int resident = (160 * 1024) / (per_tile + 64);   // workgroups a CU can hold by LDS
+    const int tpg = kWaves;
+    const int lds = (D / 16) * 4 * 1024 * MT + MT * 32 * 8;
+    int resident = (160 * 1024) / lds;                // workgroups a CU can hold by LDS
     if (resident > 8) resident = 8;
     if (resident < 1) resident = 1;
-    const int64_t target = 256LL * resident;            // 256 compute units
-    int64_t gx = (ntiles + kWaves - 1) / kWaves;
-    const int64_t others = (int64_t)groups * P;
-    int64_t cap = target / others;
+    const int64_t target = 256LL * resident;           // 256 compute units
+    int64_t gx = (ntiles + tpg - 1) / tpg;
+    int64_t cap = target / ((int64_t)groups_y * P);
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT>), dim3((unsigned)gx, groups, P),
+    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();

@@ -142,8 +142,9 @@ int tq_score_with_kernel(const float* A, const float* T, const tq_keys* keys,
 /*
  * tq_score_kernel_name: name of the kernel tq_score_with_kernel would launch
  * for this shape and format, or NULL if unsupported. Host-only, no GPU work.
+ * The returned string is static.
  */
-const char* tq_score_kernel_name(int layout, int bits, int C, int B, int D, int kernel);
+const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int S, int D, int kernel);
 
 /*
  * tq_decode_debug: expand keys of either layout into the unpacked layout,

@@ -32,7 +32,7 @@ def test_workload_full_size(name):
     w = synth.workload(name)
     say(f"workload {name}: building inputs {w.describe()}")
     inp = ow.make_inputs(w)
-    kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.B, w.D)
+    kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D)
     say(f"workload {name}: GPU transform + score, kernel {kname}")
     A, T = tq.tq_query_transform(t(inp.q), t(inp.Pi), t(inp.S_mat))
     keys = keys_to_gpu(w.layout, w.bits, inp.idx, inp.sign, inp.gamma_k)
@@ -59,4 +59,4 @@ def test_workload_full_size(name):
 @pytest.mark.parametrize("name", ["decode", "packed", "gqa", "long"])
 def test_workloads_run_on_matrix_cores(name):
     w = synth.workload(name)
-    assert tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.B, w.D).startswith("mfma")
+    assert tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D).startswith("mfma")
