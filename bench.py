@@ -55,7 +55,50 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 256 MiB device buffer 20 times (known bytes, to scale "
+                         "memory counters read under a profiler), then exit")
     return ap.parse_args()
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "tq_score_decode_counters.json")
+
+
+def measured_traffic(w, kname):
+    """HBM bytes per score launch from the committed counter record, if it was taken
+    on this workload with the kernel source as it is now; else None."""
+    import hashlib
+
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for p in rec["source_files"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    if h.hexdigest() != rec.get("source_sha256") or w.name != "decode" or "mfma32_unpacked_mt1" not in rec["kernel"] \
+            or kname != "mfma32_unpacked_mt1":
+        return None
+    return rec["per_dispatch"]["traffic_bytes"]
+
+
+def copy_calibration() -> int:
+    """Device-to-device copies of a known size, for calibrating FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    n = 256 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                                           "copies": 20}}), flush=True)
+    return 0
 
 
 def build_ring(w, device, seed_base):
@@ -203,6 +246,8 @@ def main() -> int:
                                    "exchange (see the design notes) but no multi-GPU run is built",
                           "n_gpus": args.gpus}), flush=True)
         return 2
+    if args.copy_calibration:
+        return copy_calibration()
     import torch
 
     import compressed_attention_scoring_amd as tq
@@ -264,7 +309,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(w, kname),
             "kernel": kname,
             "bytes_per_launch": alg_bytes,
             "avg_launch_us": score_us,
