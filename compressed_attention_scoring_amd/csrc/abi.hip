@@ -48,14 +48,27 @@ tq::KeyStreams streams(const tq_keys* k) {
                           k->gamma};
 }
 
-bool mfma_ok(int layout, int bits, int C, int B, int D) {
-    return tq::score_mfma_supported(layout, layout == TQ_PACKED ? bits : 0, C, B, D);
+// The matrix-core kernels address one 32-query tile of scores with 32-bit
+// byte offsets below 2^31, so they take S < 2^24 keys per problem.
+constexpr int kMfmaMaxKeys = 1 << 24;
+
+int mfma_variant(int kernel) {
+    return kernel == TQ_KERNEL_MFMA_LDS ? tq::kMfmaLds : kernel == TQ_KERNEL_MFMA_REG ? tq::kMfmaReg : tq::kMfmaAuto;
+}
+
+bool is_mfma(int kernel) {
+    return kernel == TQ_KERNEL_MFMA || kernel == TQ_KERNEL_MFMA_LDS || kernel == TQ_KERNEL_MFMA_REG;
+}
+
+bool mfma_ok(int layout, int bits, int C, int B, int S, int D, int kernel = TQ_KERNEL_MFMA) {
+    return S < kMfmaMaxKeys &&
+           tq::score_mfma_supported(layout, layout == TQ_PACKED ? bits : 0, C, B, D, mfma_variant(kernel));
 }
 
 // Default choice: the matrix-core family wherever it applies, the vector
 // family for everything else (odd D, codebooks over 8 entries).
-int pick_kernel(int layout, int bits, int C, int B, int D) {
-    return mfma_ok(layout, bits, C, B, D) ? TQ_KERNEL_MFMA : TQ_KERNEL_VALU;
+int pick_kernel(int layout, int bits, int C, int B, int S, int D) {
+    return mfma_ok(layout, bits, C, B, S, D) ? TQ_KERNEL_MFMA : TQ_KERNEL_VALU;
 }
 
 }  // namespace
@@ -93,10 +106,12 @@ const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int 
     if (layout == TQ_PACKED && ((bits != 2 && bits != 3) || D % 8 || C != (1 << bits))) return nullptr;
     if (layout == TQ_UNPACKED && (C < 1 || C > 256)) return nullptr;
     const int b = layout == TQ_PACKED ? bits : 0;
-    if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(layout, bits, C, B, D);
+    if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(layout, bits, C, B, S, D);
     if (kernel == TQ_KERNEL_VALU)
         return layout == TQ_UNPACKED ? "valu_unpacked" : bits == 2 ? "valu_packed2" : "valu_packed3";
-    if (kernel == TQ_KERNEL_MFMA) return tq::score_mfma_name(layout, b, C, B, D);
+    if (is_mfma(kernel))
+        return mfma_ok(layout, bits, C, B, S, D, kernel) ? tq::score_mfma_name(layout, b, C, B, D, mfma_variant(kernel))
+                                                         : nullptr;
     return nullptr;
 }
 
@@ -105,7 +120,7 @@ int tq_score_with_kernel(const float* A, const float* T, const tq_keys* keys, co
     if (P < 0 || B < 0 || S < 0) return TQ_ERR_ARG;
     int kc = check_format(keys, C, D, true);
     if (kc != TQ_OK) return kc;
-    if (kernel != TQ_KERNEL_AUTO && kernel != TQ_KERNEL_VALU && kernel != TQ_KERNEL_MFMA) return TQ_ERR_ARG;
+    if (kernel != TQ_KERNEL_AUTO && kernel != TQ_KERNEL_VALU && !is_mfma(kernel)) return TQ_ERR_ARG;
     if (P == 0 || B == 0 || S == 0) return TQ_OK;   // empty call: nothing to launch
     if (!A || !T || !codebook || !scores) return TQ_ERR_ARG;
     kc = check_buffers(keys, P, S, D);
@@ -113,12 +128,13 @@ int tq_score_with_kernel(const float* A, const float* T, const tq_keys* keys, co
     if (B > 262144 || !fits(P, B, S) || !fits(P, B, D)) return TQ_ERR_UNSUPPORTED;
     if (!aligned16(A) || !aligned16(T) || !aligned16(codebook) || !aligned16(scores)) return TQ_ERR_ALIGN;
     const int bits = keys->layout == TQ_PACKED ? keys->bits : 0;
-    if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(keys->layout, bits, C, B, D);
+    if (kernel == TQ_KERNEL_AUTO) kernel = pick_kernel(keys->layout, bits, C, B, S, D);
     hipError_t e;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (kernel == TQ_KERNEL_MFMA) {
-        if (!mfma_ok(keys->layout, bits, C, B, D)) return TQ_ERR_UNSUPPORTED;
-        e = tq::launch_score_mfma(A, T, streams(keys), keys->layout, bits, codebook, C, scores, P, B, S, D, st);
+    if (is_mfma(kernel)) {
+        if (!mfma_ok(keys->layout, bits, C, B, S, D, kernel)) return TQ_ERR_UNSUPPORTED;
+        e = tq::launch_score_mfma(A, T, streams(keys), keys->layout, bits, codebook, C, scores, P, B, S, D,
+                                  mfma_variant(kernel), st);
     } else if (kernel == TQ_KERNEL_VALU) {
         e = tq::launch_score_valu(A, T, streams(keys), keys->layout, bits, codebook, C, scores, P, B, S, D, st);
     } else {

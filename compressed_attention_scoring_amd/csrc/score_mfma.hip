@@ -357,6 +357,63 @@ __device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
     lo = __builtin_bit_cast(uint16_t, l);
 }
 
+// Score stores go through a raw buffer descriptor covering the valid rows of one
+// 32-query tile of the output, so the hardware drops writes to rows past B.
+// Keys past S get a lane offset of 2^31, beyond any descriptor here. Every store
+// therefore issues on every path, with no branches, which keeps the compiler's
+// count of outstanding memory operations exact: a wait for the next tile's codes
+// does not also wait for this tile's stores to reach memory.
+// Byte offsets are row * S * 4 + key * 4 with row < 32; the caller keeps
+// S < 2^24, so every in-range offset is below 2^31 and an out-of-range key's
+// offset (2^31 plus a row offset below 2^31) cannot wrap around.
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit buffer, gfx9 family
+constexpr uint32_t kDropKey = 0x80000000u;       // lane offset of a key past S
+constexpr int kNonTemporal = 2;                  // cache policy: stream past the caches
+
+// Byte offset of this lane's key in row 4 * g of a tile (g = lane / 32), or
+// kDropKey past the last key; output element v then adds row_offset(v, S).
+__device__ __forceinline__ uint32_t lane_offset(int s, int S, int g) {
+    return s < S ? ((uint32_t)g * 4u * (uint32_t)S + (uint32_t)s) * 4u : kDropKey;
+}
+// Rows 8 (v / 4) + (v % 4) of the MFMA output element v, in bytes; uniform.
+__device__ __forceinline__ uint32_t row_offset(int v, int S) {
+    return (uint32_t)(8 * (v >> 2) + (v & 3)) * (uint32_t)S * 4u;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t score_rows(float* base, int rows, int S) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)((uint32_t)rows * (uint32_t)S * 4u), kBufferWord3);
+}
+
+__device__ __forceinline__ void store_score(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kNonTemporal);
+}
+
+// Codebook byte tables for lut4: the entries (up to 8, zero beyond C) times a
+// power of two sc, split into f16 hi and lo parts.
+__device__ __forceinline__ void codebook_tables(const float* __restrict__ codebook, int C, float& sc,
+                                                uint32_t (&tab_hi)[4], uint32_t (&tab_lo)[4]) {
+    float cbv[8];
+    float mc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        cbv[k] = k < C ? codebook[k] : 0.f;
+        mc = fmaxf(mc, fabsf(cbv[k]));
+    }
+    sc = pow2_scale_for(mc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) tab_hi[w] = tab_lo[w] = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        uint16_t hb, lb;
+        split_f16(cbv[k] * sc, hb, lb);
+        const int w = k >> 2, sh = 8 * (k & 3);
+        tab_hi[w] |= (uint32_t)(hb & 0xffu) << sh;
+        tab_hi[2 + w] |= (uint32_t)(hb >> 8) << sh;
+        tab_lo[w] |= (uint32_t)(lb & 0xffu) << sh;
+        tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
+    }
+}
+
 // One 32-key tile's compressed codes for this lane: its segment of the key's
 // index and sign streams, and the key's gamma.
 template <int NI, int NS>
@@ -365,6 +422,26 @@ struct TileCodes {
     uint32_t sw[NS];
     float gam;
 };
+
+// Key-side operands of k-step j: codebook hi and lo parts looked up by index,
+// and signs as f16 +-1.
+template <int LAYOUT, int BITS, int NI, int NS>
+__device__ __forceinline__ void key_operands(const TileCodes<NI, NS>& c, int j, const uint32_t (&tab_hi)[4],
+                                             const uint32_t (&tab_lo)[4], Op8& chi, Op8& clo, Op8& sg) {
+    using F = Fmt<LAYOUT, BITS>;
+    uint32_t x0, x1;
+    F::template selectors<NI>(c.iw, j, x0, x1);
+    lut4(x0, tab_hi, chi.u[0], chi.u[1]);
+    lut4(x1, tab_hi, chi.u[2], chi.u[3]);
+    lut4(x0, tab_lo, clo.u[0], clo.u[1]);
+    lut4(x1, tab_lo, clo.u[2], clo.u[3]);
+    F::template signs<NS>(c.sw, j, sg.u);
+}
+
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kValuPerMfma = 7;
 
 // Segment m (0 or 1) of a key: coordinates [m*D/2, (m+1)*D/2).
 template <int LAYOUT, int BITS, int D>
@@ -408,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps the tile loop scalar
     const int p = blockIdx.z;
     const int b0 = blockIdx.y * MT * 32;
     const int rows = min(MT * 32, B - b0);
@@ -457,26 +534,9 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             const int s = min(min(tile, ntiles - 1) * kTileKeys + col, S - 1);
             load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
             asm volatile("" ::: "memory");
-            // codebook: power-of-two scale, f16 hi/lo split, byte tables. Its loads
-            // come after the vector loads above so their latency is not paid first.
-            float cbv[8];
-            float mc = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                cbv[k] = k < C ? codebook[k] : 0.f;
-                mc = fmaxf(mc, fabsf(cbv[k]));
-            }
-            sc = pow2_scale_for(mc);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                uint16_t hb, lb;
-                split_f16(cbv[k] * sc, hb, lb);
-                const int w = k >> 2, sh = 8 * (k & 3);
-                tab_hi[w] |= (uint32_t)(hb & 0xffu) << sh;
-                tab_hi[2 + w] |= (uint32_t)(hb >> 8) << sh;
-                tab_lo[w] |= (uint32_t)(lb & 0xffu) << sh;
-                tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
-            }
+            // codebook tables; their loads come after the vector loads above so
+            // their latency is not paid first
+            codebook_tables(codebook, C, sc, tab_hi, tab_lo);
         }
         if (row >= rows) {
 #pragma unroll
@@ -521,7 +581,6 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     }
     __syncthreads();
 
-    float* out_p = scores + ((int64_t)p * B + b0) * S;
     const uint8_t* my_ops = ops + lane * 16;
 
     while (tile < ntiles) {
@@ -568,24 +627,194 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        const int s = tile * kTileKeys + col;
-        if (s < S) {
+        const uint32_t lo = lane_offset(tile * kTileKeys + col, S, g);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
+            const __amdgpu_buffer_rsrc_t out_r =
+                score_rows(scores + ((int64_t)p * B + b0 + mt * 32) * S, max(0, min(32, rows - mt * 32)), S);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-                    if (row < rows) {
-                        const float2 k = rowk[row];
-                        // scores are written once and not read again here: stream them past the caches
-                        __builtin_nontemporal_store(fmaf(k.y * cur.gam, accR[mt][v], accM[mt][v] * k.x),
-                                                    out_p + (int64_t)row * S + s);
-                    }
-                }
+            for (int v = 0; v < 16; ++v) {
+                const float2 k = rowk[mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3)];
+                store_score(out_r, lo + row_offset(v, S), fmaf(k.y * cur.gam, accR[mt][v], accM[mt][v] * k.x));
             }
         }
         cur = nxt;
         tile = next;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Query-stationary variant: each wavefront keeps one 32-query tile's operands
+// (A_hi, A_lo, T_hi, T_lo: 4 x D/16 x 16 bytes per lane) in registers for its
+// whole life and streams key tiles past them, so the main loop touches LDS only
+// for the 32 per-row epilogue factors and needs no workgroup barrier. A lane
+// builds its own operands: row lane % 32, coordinate half lane / 32, which is
+// exactly the slice of A and T that the MFMA A-operand layout gives it. The
+// QW wavefronts of a workgroup that hold different query tiles (B > 32) walk
+// the same key tiles, so a key tile's bytes come from HBM once per workgroup and
+// from the L1 cache for the others.
+// ---------------------------------------------------------------------------
+template <int LAYOUT, int BITS, int D, int QT, int QW, int MINW>
+__global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
+    const float* __restrict__ A, const float* __restrict__ T,
+    const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+    const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
+    float* __restrict__ scores, int B, int S, float coef) {
+    using F = Fmt<LAYOUT, BITS>;
+    constexpr int HALF = D / 2;
+    constexpr int KS = D / 16;
+    constexpr int NI = F::template idx_dw<D>();
+    constexpr int NS = F::template sign_dw<D>();
+    constexpr int KW = kWaves / QW;            // key-tile streams per workgroup
+    constexpr int VPM = QT == 1 ? kValuPerMfma : (kValuPerMfma + 1) / 2;
+
+    __shared__ float2 rowk[kWaves][QT * 32];   // per-row epilogue factors (M, R) of each wavefront
+
+    const int lane = threadIdx.x & 63;
+    // the wavefront index is uniform; saying so keeps everything derived from it
+    // (query tiles, output descriptors) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.z;
+    const int b0 = (blockIdx.y * QW + wave % QW) * (QT * 32);
+    if (b0 >= B) return;                       // no barrier follows: idle wavefronts just leave
+    const int rows = min(QT * 32, B - b0);
+    const int col = lane & 31;
+    const int g = lane >> 5;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    const int64_t key0 = (int64_t)p * S;
+    int tile = blockIdx.x * KW + wave / QW;
+    const int stride = gridDim.x * KW;
+    if (tile >= ntiles) return;
+
+    // this lane's half rows of A and T (row col of each query tile, clamped:
+    // rows past B are computed but never stored)
+    float a[QT][HALF], t[QT][HALF];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int64_t roff = ((int64_t)p * B + b0 + min(qt * 32 + col, rows - 1)) * D + g * HALF;
+#pragma unroll
+        for (int k = 0; k < HALF; k += 4) {
+            const float4 va = *reinterpret_cast<const float4*>(A + roff + k);
+            const float4 vt = *reinterpret_cast<const float4*>(T + roff + k);
+            a[qt][k] = va.x; a[qt][k + 1] = va.y; a[qt][k + 2] = va.z; a[qt][k + 3] = va.w;
+            t[qt][k] = vt.x; t[qt][k + 1] = vt.y; t[qt][k + 2] = vt.z; t[qt][k + 3] = vt.w;
+        }
+    }
+    // first tile's codes right behind A and T (see score_mfma_kernel for why the
+    // loads are unconditional and fenced)
+    TileCodes<NI, NS> cur;
+    asm volatile("" ::: "memory");
+    {
+        const int s = min(tile * kTileKeys + col, S - 1);
+        load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
+    }
+    asm volatile("" ::: "memory");
+    float sc;
+    uint32_t tab_hi[4], tab_lo[4];
+    codebook_tables(codebook, C, sc, tab_hi, tab_lo);
+
+    // per-row powers of two (a row's two halves sit in lanes col and col + 32),
+    // then the f16 hi/lo operands in contraction order
+    Op8 ahi[QT][KS], alo[QT][KS], thi[QT][KS], tlo[QT][KS];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        float ma = 0.f, mt = 0.f;
+#pragma unroll
+        for (int k = 0; k < HALF; ++k) {
+            ma = fmaxf(ma, fabsf(a[qt][k]));
+            mt = fmaxf(mt, fabsf(t[qt][k]));
+        }
+        ma = fmaxf(ma, __shfl_xor(ma, 32));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float sA = pow2_scale_for(ma);
+        const float sT = pow2_scale_for(mt);
+        if (g == 0) rowk[wave][qt * 32 + col] = make_float2(1.f / (sA * sc), coef / sT);
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xa = a[qt][mse_dim<LAYOUT, BITS>(j, e)] * sA;
+                const _Float16 ha = (_Float16)xa;
+                ahi[qt][j].h[e] = ha;
+                alo[qt][j].h[e] = (_Float16)(xa - (float)ha);
+                const float xt = t[qt][qjl_dim<LAYOUT>(j, e)] * sT;
+                const _Float16 ht = (_Float16)xt;
+                thi[qt][j].h[e] = ht;
+                tlo[qt][j].h[e] = (_Float16)(xt - (float)ht);
+            }
+        }
+    }
+    // rowk is read back by other lanes of this wavefront only; LDS operations of
+    // one wavefront complete in order
+    __builtin_amdgcn_wave_barrier();
+
+    __amdgpu_buffer_rsrc_t out_r[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+        out_r[qt] = score_rows(scores + ((int64_t)p * B + b0 + qt * 32) * S, max(0, min(32, rows - qt * 32)), S);
+
+    // One tile: the key-side operands of k-step j + 1 are built while the MFMAs
+    // of step j run (the scheduling groups below interleave each MFMA with a few
+    // vector instructions), then the scores are scaled and stored.
+    auto tile_scores = [&](const TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
+        f32x16 accM[QT], accR[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { accM[qt][v] = 0.f; accR[qt][v] = 0.f; }
+        }
+        Op8 chi[2], clo[2], sg[2];
+        key_operands<LAYOUT, BITS, NI, NS>(c, 0, tab_hi, tab_lo, chi[0], clo[0], sg[0]);
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int u = j & 1;
+            if (j + 1 < KS) key_operands<LAYOUT, BITS, NI, NS>(c, j + 1, tab_hi, tab_lo, chi[u ^ 1], clo[u ^ 1], sg[u ^ 1]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                accM[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[qt][j].h, chi[u].h, accM[qt], 0, 0, 0);
+                accR[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[qt][j].h, sg[u].h, accR[qt], 0, 0, 0);
+                accM[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[qt][j].h, chi[u].h, accM[qt], 0, 0, 0);
+                accR[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[qt][j].h, sg[u].h, accR[qt], 0, 0, 0);
+                accM[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[qt][j].h, clo[u].h, accM[qt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 5 * QT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint32_t lo = lane_offset(t * kTileKeys + col, S, g);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float2 k = rowk[wave][qt * 32 + 8 * (v >> 2) + 4 * g + (v & 3)];
+                store_score(out_r[qt], lo + row_offset(v, S), fmaf(k.y * c.gam, accR[qt][v], accM[qt][v] * k.x));
+            }
+        }
+    };
+
+    // Two code buffers in turn (no register copies between iterations, so a wait
+    // for one buffer never waits for the other's loads); the next tile's codes
+    // are requested before the current tile is computed, clamped and
+    // unconditional like the first load.
+    TileCodes<NI, NS> nxt;
+    while (true) {
+        {
+            const int s = min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1);
+            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma, key0 + s, g);
+        }
+        tile_scores(cur, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+        {
+            const int s = min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1);
+            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
+        }
+        tile_scores(nxt, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
     }
 }
 
@@ -628,6 +857,69 @@ hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* 
     return hipGetLastError();
 }
 
+// Query-stationary launch: each wavefront holds QT query tiles; a workgroup's
+// four wavefronts cover QW groups of QT query tiles times 4 / QW key-tile
+// streams; MINW wavefronts per SIMD are resident, so 256 * MINW workgroups fill
+// the chip.
+template <int LAYOUT, int BITS, int D, int QT, int QW, int MINW>
+hipError_t launch_qs_cfg(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                         float* scores, int P, int B, int S, hipStream_t stream) {
+    constexpr int KW = kWaves / QW;
+    const int qgroups = (B + QT * 32 - 1) / (QT * 32);
+    const int groups_y = (qgroups + QW - 1) / QW;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    int64_t gx = (ntiles + KW - 1) / KW;
+    int64_t cap = 256LL * MINW / ((int64_t)groups_y * P);
+    if (cap < 1) cap = 1;
+    if (gx > cap) gx = cap;
+    const float coef = (float)(kSqrtHalfPi / (double)D);
+    hipLaunchKernelGGL((score_qs_kernel<LAYOUT, BITS, D, QT, QW, MINW>), dim3((unsigned)gx, groups_y, P),
+                       dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
+                       scores, B, S, coef);
+    return hipGetLastError();
+}
+
+
+int qw_for(int B, int qt) {
+    const int groups = (B + qt * 32 - 1) / (qt * 32);
+    return groups >= 3 ? 4 : groups;
+}
+
+template <int LAYOUT, int BITS, int D, int QT>
+hipError_t launch_qs_qt(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                        float* scores, int P, int B, int S, hipStream_t stream) {
+    constexpr int MINW = QT == 2 ? 1 : (D <= 64 ? 2 : (LAYOUT == 0 ? 1 : 2));   // fits the registers
+    switch (qw_for(B, QT)) {
+        case 4: return launch_qs_cfg<LAYOUT, BITS, D, QT, 4, MINW>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 2: return launch_qs_cfg<LAYOUT, BITS, D, QT, 2, MINW>(A, T, k, codebook, C, scores, P, B, S, stream);
+        default: return launch_qs_cfg<LAYOUT, BITS, D, QT, 1, MINW>(A, T, k, codebook, C, scores, P, B, S, stream);
+    }
+}
+
+// One query tile per wavefront. Two (QT = 2, 400 registers, one wavefront per
+// SIMD) halve the key decoding per MFMA but measured slower on the 128-query
+// workloads than two wavefronts per SIMD with one tile each.
+template <int LAYOUT, int BITS, int D>
+hipError_t launch_qs_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                       float* scores, int P, int B, int S, hipStream_t stream) {
+    return launch_qs_qt<LAYOUT, BITS, D, 1>(A, T, k, codebook, C, scores, P, B, S, stream);
+}
+
+template <int LAYOUT, int BITS>
+hipError_t launch_qs_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
+                            int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
+    switch (D) {
+        case 32:
+            if constexpr (LAYOUT == 0)
+                return launch_qs_d<LAYOUT, BITS, 32>(A, T, k, codebook, C, scores, P, B, S, stream);
+            break;
+        case 64: return launch_qs_d<LAYOUT, BITS, 64>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 128: return launch_qs_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int LAYOUT, int BITS, int D>
 hipError_t launch_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                     float* scores, int P, int B, int S, hipStream_t stream) {
@@ -661,16 +953,42 @@ hipError_t launch_layout(const float* A, const float* T, KeyStreams k, const flo
 
 }  // namespace
 
-bool score_mfma_supported(int layout, int bits, int C, int B, int D) {
-    (void)B;
+namespace {
+
+bool lds_supported(int layout, int bits, int C, int D) {
     if (C < 1 || C > 8) return false;          // byte-select lookup tables hold 8 entries
     if (layout == 0) return D == 32 || D == 64 || D == 128 || D == 256;
     if (bits != 2 && bits != 3) return false;
     return D == 64 || D == 128 || D == 256;
 }
 
-const char* score_mfma_name(int layout, int bits, int C, int B, int D) {
-    if (!score_mfma_supported(layout, bits, C, B, D)) return nullptr;
+bool reg_supported(int layout, int bits, int C, int D) {
+    return lds_supported(layout, bits, C, D) && D <= 128;   // D = 256 would need 256 operand registers
+}
+
+// Automatic choice, from measurements on the five workload shapes: with a single
+// 32-query tile (B <= 32) the workgroup-shared LDS staging wins (its one-time
+// operand build is split over 256 threads); with more query tiles the
+// register-resident operands win (no LDS traffic in the main loop).
+int pick_variant(int layout, int bits, int C, int B, int D) {
+    if (B > 32 && reg_supported(layout, bits, C, D)) return kMfmaReg;
+    return kMfmaLds;
+}
+
+}  // namespace
+
+bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant) {
+    (void)B;
+    if (variant == kMfmaAuto) return lds_supported(layout, bits, C, D);
+    if (variant == kMfmaLds) return lds_supported(layout, bits, C, D);
+    if (variant == kMfmaReg) return reg_supported(layout, bits, C, D);
+    return false;
+}
+
+const char* score_mfma_name(int layout, int bits, int C, int B, int D, int variant) {
+    if (!score_mfma_supported(layout, bits, C, B, D, variant)) return nullptr;
+    if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, D);
+    if (variant == kMfmaReg) return layout == 0 ? "mfma32reg_unpacked" : bits == 2 ? "mfma32reg_packed2" : "mfma32reg_packed3";
     const int mt = mt_for(B, D);
     if (layout == 0) return mt == 4 ? "mfma32_unpacked_mt4" : mt == 2 ? "mfma32_unpacked_mt2" : "mfma32_unpacked_mt1";
     if (bits == 2) return mt == 4 ? "mfma32_packed2_mt4" : mt == 2 ? "mfma32_packed2_mt2" : "mfma32_packed2_mt1";
@@ -679,8 +997,15 @@ const char* score_mfma_name(int layout, int bits, int C, int B, int D) {
 
 hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              int layout, int bits, const float* codebook, int C,
-                             float* scores, int P, int B, int S, int D,
+                             float* scores, int P, int B, int S, int D, int variant,
                              hipStream_t stream) {
+    if (!score_mfma_supported(layout, bits, C, B, D, variant)) return hipErrorInvalidValue;
+    if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, D);
+    if (variant == kMfmaReg) {
+        if (layout == 0) return launch_qs_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        if (bits == 2) return launch_qs_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        return launch_qs_layout<1, 3>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+    }
     if (layout == 0) return launch_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
     if (bits == 2) return launch_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
     return launch_layout<1, 3>(A, T, keys, codebook, C, scores, P, B, S, D, stream);

@@ -35,12 +35,17 @@ hipError_t launch_score_valu(const float* A, const float* T, KeyStreams keys,
                              float* scores, int P, int B, int S, int D,
                              hipStream_t stream);
 
-// Returns false if the MFMA kernels do not cover (layout, bits, C, B, D).
-bool score_mfma_supported(int layout, int bits, int C, int B, int D);
-const char* score_mfma_name(int layout, int bits, int C, int B, int D);
+// Matrix-core kernels come in two variants that differ in where the query-side
+// operands live: staged once per workgroup in LDS, or held in each wavefront's
+// registers. kMfmaAuto picks by shape.
+enum MfmaVariant { kMfmaAuto = 0, kMfmaLds = 1, kMfmaReg = 2 };
+
+// Returns false if the variant does not cover (layout, bits, C, B, D).
+bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant);
+const char* score_mfma_name(int layout, int bits, int C, int B, int D, int variant);
 hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              int layout, int bits, const float* codebook, int C,
-                             float* scores, int P, int B, int S, int D,
+                             float* scores, int P, int B, int S, int D, int variant,
                              hipStream_t stream);
 
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,

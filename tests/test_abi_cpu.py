@@ -42,12 +42,20 @@ def test_kernel_names_host_only():
     assert n("unpacked", 0, 4, 1, 32, 32768, 128) == "mfma32_unpacked_mt1"
     assert n("packed", 2, 4, 1, 32, 131072, 128) == "mfma32_packed2_mt1"
     assert n("packed", 3, 8, 128, 4, 32768, 128) == "mfma32_packed3_mt1"
-    assert n("packed", 3, 8, 1, 128, 262144, 128) == "mfma32_packed3_mt4"
+    assert n("packed", 3, 8, 1, 128, 262144, 128) == "mfma32reg_packed3"
+    assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_lds") == "mfma32_packed3_mt4"
+    assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_reg") == "mfma32reg_packed3"
+    assert n("unpacked", 0, 4, 1, 32, 32768, 128, "mfma_reg") == "mfma32reg_unpacked"
+    assert n("unpacked", 0, 4, 1, 128, 100, 256) == "mfma32_unpacked_mt2"     # D = 256: LDS staging only
+    assert n("unpacked", 0, 4, 1, 128, 100, 256, "mfma_reg") is None
+    assert n("unpacked", 0, 4, 1, 32, 1 << 24, 128) == "valu_unpacked"        # S past the MFMA offset range
+    assert n("unpacked", 0, 4, 1, 32, 1 << 24, 128, "mfma") is None
     assert n("unpacked", 0, 4, 1, 1, 2, 2) == "valu_unpacked"
     assert n("unpacked", 0, 16, 1, 32, 100, 128) == "valu_unpacked"
     assert n("unpacked", 0, 4, 1, 32, 100, 128, "valu") == "valu_unpacked"
     assert n("unpacked", 0, 4, 1, 32, 100, 128, "mfma") == "mfma32_unpacked_mt1"
-    assert n("unpacked", 0, 4, 1, 64, 100, 128, "mfma") == "mfma32_unpacked_mt2"
+    assert n("unpacked", 0, 4, 1, 64, 100, 128, "mfma") == "mfma32reg_unpacked"
+    assert n("unpacked", 0, 4, 1, 64, 100, 128, "mfma_lds") == "mfma32_unpacked_mt2"
     assert n("packed", 2, 4, 1, 32, 100, 48, "mfma") is None
     assert n("packed", 2, 8, 1, 32, 100, 128) is None      # C != 2^bits
     assert n("packed", 4, 16, 1, 32, 100, 128) is None     # 4-bit not supported
@@ -69,7 +77,9 @@ def test_score_rejects_bad_arguments_before_launch():
     assert _score(_keys(layout=5)) == ARG
     assert _score(_keys(), S=-1) == ARG
     assert _score(_keys(), D=0) == ARG
-    assert _score(_keys(), kernel=3) == ARG
+    assert _score(_keys(), kernel=5) == ARG
+    assert _score(_keys(), kernel=-1) == ARG
+    assert _score(_keys(), S=1 << 24, kernel=2) == UNSUP
     assert _score(_keys(layout=1, bits=4), C=16) == UNSUP
     assert _score(_keys(layout=1, bits=2), C=8) == UNSUP
     assert _score(_keys(layout=1, bits=3), C=8, D=12) == UNSUP

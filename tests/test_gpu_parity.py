@@ -83,11 +83,12 @@ def test_query_transform_parity(P, H, B, D):
 SCORE_CASES = []
 for layout, bits, C in (("unpacked", 0, 4), ("unpacked", 0, 8), ("packed", 2, 4), ("packed", 3, 8)):
     for D in ((32, 64, 128, 256) if layout == "unpacked" else (64, 128, 256)):
-        for B, S in ((1, 1), (2, 31), (4, 33), (5, 257), (32, 300), (33, 64), (64, 100), (128, 95)):
+        for B, S in ((1, 1), (2, 31), (4, 33), (5, 257), (32, 300), (33, 64), (64, 100), (96, 70), (128, 95),
+                     (161, 40)):
             SCORE_CASES.append((layout, bits, C, D, B, S))
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg"])
 @pytest.mark.parametrize("layout,bits,C,D,B,S", SCORE_CASES)
 def test_score_random_codes(kernel, layout, bits, C, D, B, S):
     if tq.tq_score_kernel_name(layout, bits, C, 2, B, S, D, kernel) is None:
@@ -119,14 +120,15 @@ def test_score_valu_odd_dims(D):
     assert rel_err(got, oracle_scores_transformed(A, T, idx_u, sign_u, gamma_k, cb)) <= SCORE_TOL
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg"])
+@pytest.mark.parametrize("B", [32, 100])
 @pytest.mark.parametrize("scale", [1e-6, 1e4, 3e5])
-def test_score_extreme_magnitudes(kernel, scale):
+def test_score_extreme_magnitudes(kernel, B, scale):
     """Large and tiny A, T (and a large codebook) stay accurate: the matrix-core
     path rescales its f16 operands by powers of two."""
-    say(f"score extreme magnitudes kernel={kernel} scale={scale}")
+    say(f"score extreme magnitudes kernel={kernel} B={B} scale={scale}")
     rng = np.random.default_rng(7)
-    P, B, S, D, C = 1, 32, 64, 128, 8
+    P, S, D, C = 1, 64, 128, 8
     A = (rng.standard_normal((P, B, D)) * scale).astype(np.float32)
     T = (rng.standard_normal((P, B, D)) * scale * 10).astype(np.float32)
     cb = (np.sort(rng.standard_normal(C)) * scale).astype(np.float32)
