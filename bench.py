@@ -61,16 +61,18 @@ def parse():
     return ap.parse_args()
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "tq_score_decode_counters.json")
+def counters_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"tq_score_{workload}_counters.json")
 
 
 def measured_traffic(w, kname):
-    """HBM bytes per score launch from the committed counter record, if it was taken
-    on this workload with the kernel source as it is now; else None."""
+    """HBM bytes per score launch from the committed counter record of this
+    workload, if it was taken on the kernel that runs now with its source as it
+    is now; else None."""
     import hashlib
 
     try:
-        with open(COUNTERS) as f:
+        with open(counters_path(w.name)) as f:
             rec = json.load(f)
         h = hashlib.sha256()
         for p in rec["source_files"]:
@@ -78,8 +80,7 @@ def measured_traffic(w, kname):
                 h.update(f.read())
     except (OSError, KeyError, ValueError):
         return None
-    if h.hexdigest() != rec.get("source_sha256") or w.name != "decode" or "mfma32_unpacked_mt1" not in rec["kernel"] \
-            or kname != "mfma32_unpacked_mt1":
+    if h.hexdigest() != rec.get("source_sha256") or rec.get("kernel_id") != kname:
         return None
     return rec["per_dispatch"]["traffic_bytes"]
 

@@ -53,11 +53,17 @@ tq::KeyStreams streams(const tq_keys* k) {
 constexpr int kMfmaMaxKeys = 1 << 24;
 
 int mfma_variant(int kernel) {
-    return kernel == TQ_KERNEL_MFMA_LDS ? tq::kMfmaLds : kernel == TQ_KERNEL_MFMA_REG ? tq::kMfmaReg : tq::kMfmaAuto;
+    switch (kernel) {
+        case TQ_KERNEL_MFMA_LDS: return tq::kMfmaLds;
+        case TQ_KERNEL_MFMA_REG: return tq::kMfmaReg;
+        case TQ_KERNEL_MFMA16: return tq::kMfmaSmall;
+        default: return tq::kMfmaAuto;
+    }
 }
 
 bool is_mfma(int kernel) {
-    return kernel == TQ_KERNEL_MFMA || kernel == TQ_KERNEL_MFMA_LDS || kernel == TQ_KERNEL_MFMA_REG;
+    return kernel == TQ_KERNEL_MFMA || kernel == TQ_KERNEL_MFMA_LDS || kernel == TQ_KERNEL_MFMA_REG ||
+           kernel == TQ_KERNEL_MFMA16;
 }
 
 bool mfma_ok(int layout, int bits, int C, int B, int S, int D, int kernel = TQ_KERNEL_MFMA) {

@@ -819,6 +819,175 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Small-batch variant (a few queries per problem): v_mfma_f32_16x16x32_f16 with the 16 keys of a
+// tile as columns and, as the 16 rows, four queries times four operand types:
+// row 4 b + type holds A_hi, A_lo, T_hi or T_lo of query b. A 32-wide
+// contraction chunk carries 16 codebook coordinates and 16 sign coordinates:
+// in each lane's 8 elements, 0-3 are codebook coordinates (zero in the T rows)
+// and 4-7 are sign coordinates (zero in the A rows). A third MFMA per k-step
+// adds A_hi c_lo over 32 coordinates into the same accumulator (only the A_hi
+// rows are non-zero in it). The output element (row 4 b + type, key) lands in
+// lane 16 b + key, register type, so a lane combines the four types of its
+// (query, key) pair by itself: 12 MFMAs of 16 cycles per 16 keys at D = 128,
+// where padding four queries to the 32-row tile costs 40 of 32 cycles per 32.
+// Lane group gq = lane / 16 owns coordinates [gq D/4, (gq + 1) D/4) of each key
+// and unpacks them in the same orders as the other variants (mse_dim and
+// qjl_dim over a D/2-coordinate half, here used on a D/4 quarter).
+// Query groups of four beyond the first (B = 5..8) are further workgroup rows.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kTileKeys16 = 16;
+
+template <int LAYOUT, int BITS, int D>
+struct SmallFmt {
+    using F = Fmt<LAYOUT, BITS>;
+    static constexpr int Q = D / 4;                            // coordinates per lane
+    static constexpr int NI = F::template idx_dw<D / 2>();     // code dwords per lane
+    static constexpr int NS = F::template sign_dw<D / 2>();
+    static constexpr int IDX_ROW = F::template idx_row<D>();
+    static constexpr int SIGN_ROW = F::template sign_row<D>();
+    static constexpr int NJ = Q / 8;                           // k-steps of 8 coordinates per lane
+};
+
+template <int LAYOUT, int BITS, int D>
+__device__ __forceinline__ void load_quarter(TileCodes<SmallFmt<LAYOUT, BITS, D>::NI, SmallFmt<LAYOUT, BITS, D>::NS>& c,
+                                             const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+                                             const void* __restrict__ gamma, int64_t key, int gq) {
+    using SF = SmallFmt<LAYOUT, BITS, D>;
+    constexpr int IQ = SF::IDX_ROW / 4, SQ = SF::SIGN_ROW / 4;
+    load_dwords<SF::NI, align_of_seg(SF::IDX_ROW, IQ)>(idx + key * SF::IDX_ROW + gq * IQ, c.iw);
+    load_dwords<SF::NS, align_of_seg(SF::SIGN_ROW, SQ)>(sign + key * SF::SIGN_ROW + gq * SQ, c.sw);
+    if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
+    else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
+}
+
+template <int LAYOUT, int BITS, int D, int MINW>
+__global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
+    const float* __restrict__ A, const float* __restrict__ T,
+    const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+    const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
+    float* __restrict__ scores, int B, int S, float coef) {
+    using SF = SmallFmt<LAYOUT, BITS, D>;
+    using F = Fmt<LAYOUT, BITS>;
+    constexpr int NI = SF::NI, NS = SF::NS, NJ = SF::NJ, Q = SF::Q;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.z;
+    const int b0 = blockIdx.y * 4;                 // this workgroup's four queries
+    const int nb = min(4, B - b0);
+    const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
+    int tile = blockIdx.x * kWaves + wave;
+    const int stride = gridDim.x * kWaves;
+    if (tile >= ntiles) return;                    // no barrier in this kernel
+    const int gq = lane >> 4;                      // lane group: coordinate quarter / output query
+    const int kc = lane & 15;                      // key column
+    const int r = lane & 15;                       // operand row = 4 b + type
+    const int rb = r >> 2, rtype = r & 3;
+    const int64_t key0 = (int64_t)p * S;
+
+    // this lane's quarter row: A for types 0-1, T for types 2-3 (query rb,
+    // clamped: queries past B are computed but never stored)
+    const float* src = (rtype < 2 ? A : T) + ((int64_t)p * B + b0 + min(rb, nb - 1)) * D + gq * Q;
+    float x[Q];
+#pragma unroll
+    for (int k = 0; k < Q; k += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + k);
+        x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
+    }
+    TileCodes<NI, NS> cur;
+    asm volatile("" ::: "memory");
+    load_quarter<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
+    asm volatile("" ::: "memory");
+    float sc;
+    uint32_t tab_hi[4], tab_lo[4];
+    codebook_tables(codebook, C, sc, tab_hi, tab_lo);
+
+    // row scale: max over the row's four quarters (lanes r, r + 16, r + 32, r + 48)
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) mx = fmaxf(mx, fabsf(x[k]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float s_row = pow2_scale_for(mx);
+    // epilogue factors of output query gq: its A scale sits in row 4 gq (lane 4 gq),
+    // its T scale in row 4 gq + 2
+    const float sA_out = __shfl(s_row, 4 * gq);
+    const float sT_out = __shfl(s_row, 4 * gq + 2);
+    const float kx = 1.f / (sA_out * sc);
+    const float ky = coef / sT_out;
+
+    // operands: for k-step j, ops[j][0] and [1] pair codebook-hi elements 0-3
+    // (coordinates mse_dim(j, 0..3) and (j, 4..7)) with sign elements 4-7
+    // (coordinates qjl_dim(j, 0..3) and (j, 4..7)); ops[j][2] is A_hi over
+    // mse_dim(j, 0..7) for the codebook-lo product.
+    Op8 ops[NJ][3];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xa = x[mse_dim<LAYOUT, BITS>(j, 4 * h + e)] * s_row;
+                const _Float16 ha = (_Float16)xa;
+                const _Float16 la = (_Float16)(xa - (float)ha);
+                const float xt = x[qjl_dim<LAYOUT>(j, 4 * h + e)] * s_row;
+                const _Float16 ht = (_Float16)xt;
+                const _Float16 lt = (_Float16)(xt - (float)ht);
+                ops[j][h].h[e] = rtype == 0 ? ha : rtype == 1 ? la : (_Float16)0.f;
+                ops[j][h].h[4 + e] = rtype == 2 ? ht : rtype == 3 ? lt : (_Float16)0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xa = x[mse_dim<LAYOUT, BITS>(j, e)] * s_row;
+            ops[j][2].h[e] = rtype == 0 ? (_Float16)xa : (_Float16)0.f;
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t out_r = score_rows(scores + ((int64_t)p * B + b0) * S, nb, S);
+
+    auto tile_scores = [&](const TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            uint32_t x0, x1;
+            F::template selectors<NI>(c.iw, j, x0, x1);
+            uint32_t sgn[4];
+            F::template signs<NS>(c.sw, j, sgn);
+            Op8 k0, k1, kl;
+            lut4(x0, tab_hi, k0.u[0], k0.u[1]);
+            k0.u[2] = sgn[0]; k0.u[3] = sgn[1];
+            lut4(x1, tab_hi, k1.u[0], k1.u[1]);
+            k1.u[2] = sgn[2]; k1.u[3] = sgn[3];
+            lut4(x0, tab_lo, kl.u[0], kl.u[1]);
+            lut4(x1, tab_lo, kl.u[2], kl.u[3]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][0].h, k0.h, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][1].h, k1.h, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][2].h, kl.h, acc, 0, 0, 0);
+        }
+        // lane 16 b + key holds rows 4 b .. 4 b + 3 of column key: the four types
+        const int s = t * kTileKeys16 + kc;
+        const uint32_t off = s < S ? ((uint32_t)gq * (uint32_t)S + (uint32_t)s) * 4u : kDropKey;
+        store_score(out_r, off, fmaf(ky * c.gam, acc[2] + acc[3], kx * (acc[0] + acc[1])));
+    };
+
+    TileCodes<NI, NS> nxt;
+    while (true) {
+        load_quarter<LAYOUT, BITS, D>(nxt, idx, sign, gamma,
+                                      key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
+        tile_scores(cur, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+        load_quarter<LAYOUT, BITS, D>(cur, idx, sign, gamma,
+                                      key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
+        tile_scores(nxt, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side: shape support and launch
 // ---------------------------------------------------------------------------
 
@@ -905,6 +1074,34 @@ hipError_t launch_qs_d(const float* A, const float* T, KeyStreams k, const float
     return launch_qs_qt<LAYOUT, BITS, D, 1>(A, T, k, codebook, C, scores, P, B, S, stream);
 }
 
+// Small-batch launch: workgroup rows are groups of four queries; MINW
+// wavefronts per SIMD are resident (the kernel needs about 100 registers at
+// D = 128), so 256 * MINW workgroups fill the chip.
+template <int LAYOUT, int BITS, int D>
+hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                          float* scores, int P, int B, int S, hipStream_t stream) {
+    constexpr int MINW = D <= 128 ? 4 : 2;
+    const int groups_y = (B + 3) / 4;
+    const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
+    int64_t gx = (ntiles + kWaves - 1) / kWaves;
+    int64_t cap = 256LL * MINW / ((int64_t)groups_y * P);
+    if (cap < 1) cap = 1;
+    if (gx > cap) gx = cap;
+    const float coef = (float)(kSqrtHalfPi / (double)D);
+    hipLaunchKernelGGL((score_mfma16_kernel<LAYOUT, BITS, D, MINW>), dim3((unsigned)gx, groups_y, P),
+                       dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
+                       scores, B, S, coef);
+    return hipGetLastError();
+}
+
+template <int LAYOUT, int BITS>
+hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
+                               int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
+    if (D == 128) return launch_small_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 256) return launch_small_d<LAYOUT, BITS, 256>(A, T, k, codebook, C, scores, P, B, S, stream);
+    return hipErrorInvalidValue;
+}
+
 template <int LAYOUT, int BITS>
 hipError_t launch_qs_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                             int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
@@ -966,11 +1163,19 @@ bool reg_supported(int layout, int bits, int C, int D) {
     return lds_supported(layout, bits, C, D) && D <= 128;   // D = 256 would need 256 operand registers
 }
 
+bool small_supported(int layout, int bits, int C, int D) {
+    return lds_supported(layout, bits, C, D) && (D == 128 || D == 256);   // a lane owns D/4 >= 32 coordinates
+}
+
 // Automatic choice, from measurements on the five workload shapes: with a single
 // 32-query tile (B <= 32) the workgroup-shared LDS staging wins (its one-time
 // operand build is split over 256 threads); with more query tiles the
 // register-resident operands win (no LDS traffic in the main loop).
 int pick_variant(int layout, int bits, int C, int B, int D) {
+    // one group of four queries: 12 16x16 MFMAs per 16 keys against 40 32x32 ones
+    // per 32 keys padded; with two groups the key decoding doubles and the
+    // padded 32x32 tile measured faster
+    if (B <= 4 && small_supported(layout, bits, C, D)) return kMfmaSmall;
     if (B > 32 && reg_supported(layout, bits, C, D)) return kMfmaReg;
     return kMfmaLds;
 }
@@ -982,6 +1187,7 @@ bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant
     if (variant == kMfmaAuto) return lds_supported(layout, bits, C, D);
     if (variant == kMfmaLds) return lds_supported(layout, bits, C, D);
     if (variant == kMfmaReg) return reg_supported(layout, bits, C, D);
+    if (variant == kMfmaSmall) return small_supported(layout, bits, C, D);
     return false;
 }
 
@@ -989,6 +1195,7 @@ const char* score_mfma_name(int layout, int bits, int C, int B, int D, int varia
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return nullptr;
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, D);
     if (variant == kMfmaReg) return layout == 0 ? "mfma32reg_unpacked" : bits == 2 ? "mfma32reg_packed2" : "mfma32reg_packed3";
+    if (variant == kMfmaSmall) return layout == 0 ? "mfma16_unpacked" : bits == 2 ? "mfma16_packed2" : "mfma16_packed3";
     const int mt = mt_for(B, D);
     if (layout == 0) return mt == 4 ? "mfma32_unpacked_mt4" : mt == 2 ? "mfma32_unpacked_mt2" : "mfma32_unpacked_mt1";
     if (bits == 2) return mt == 4 ? "mfma32_packed2_mt4" : mt == 2 ? "mfma32_packed2_mt2" : "mfma32_packed2_mt1";
@@ -1001,6 +1208,11 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              hipStream_t stream) {
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return hipErrorInvalidValue;
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, D);
+    if (variant == kMfmaSmall) {
+        if (layout == 0) return launch_small_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        if (bits == 2) return launch_small_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        return launch_small_layout<1, 3>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+    }
     if (variant == kMfmaReg) {
         if (layout == 0) return launch_qs_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
         if (bits == 2) return launch_qs_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);

@@ -129,12 +129,16 @@ int tq_score(const float* A, const float* T, const tq_keys* keys,
 #define TQ_KERNEL_VALU   1  /* any shape: one key per lane, fp32 FMAs */
 #define TQ_KERNEL_MFMA   2  /* C <= 8 and D in {64, 128, 256} (also 32 when unpacked),
                                S < 2^24: split-f16 matrix-core contraction; picks one
-                               of the two variants below by shape */
+                               of the variants below by shape */
 #define TQ_KERNEL_MFMA_LDS 3  /* matrix cores, query operands staged once per
                                  workgroup in LDS (the MFMA shapes above) */
 #define TQ_KERNEL_MFMA_REG 4  /* matrix cores, query operands held in each
                                  wavefront's registers (the MFMA shapes above
                                  with D <= 128) */
+#define TQ_KERNEL_MFMA16   5  /* matrix cores, 16x16 tiles of four queries times
+                                 their four operand rows (the MFMA shapes above
+                                 with D in {128, 256}); the automatic choice for
+                                 B <= 4 */
 
 /*
  * tq_score_with_kernel: tq_score with an explicit kernel family, so that every

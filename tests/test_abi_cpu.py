@@ -41,7 +41,13 @@ def test_kernel_names_host_only():
     n = tq.tq_score_kernel_name
     assert n("unpacked", 0, 4, 1, 32, 32768, 128) == "mfma32_unpacked_mt1"
     assert n("packed", 2, 4, 1, 32, 131072, 128) == "mfma32_packed2_mt1"
-    assert n("packed", 3, 8, 128, 4, 32768, 128) == "mfma32_packed3_mt1"
+    assert n("packed", 3, 8, 128, 4, 32768, 128) == "mfma16_packed3"
+    assert n("packed", 3, 8, 128, 4, 32768, 128, "mfma_lds") == "mfma32_packed3_mt1"
+    assert n("unpacked", 0, 4, 1, 4, 100, 128) == "mfma16_unpacked"
+    assert n("unpacked", 0, 4, 1, 5, 100, 128) == "mfma32_unpacked_mt1"
+    assert n("unpacked", 0, 4, 1, 8, 100, 128, "mfma16") == "mfma16_unpacked"
+    assert n("unpacked", 0, 4, 1, 4, 100, 64) == "mfma32_unpacked_mt1"        # 16x16 tiles need D >= 128
+    assert n("unpacked", 0, 4, 1, 4, 100, 64, "mfma16") is None
     assert n("packed", 3, 8, 1, 128, 262144, 128) == "mfma32reg_packed3"
     assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_lds") == "mfma32_packed3_mt4"
     assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_reg") == "mfma32reg_packed3"
@@ -77,7 +83,7 @@ def test_score_rejects_bad_arguments_before_launch():
     assert _score(_keys(layout=5)) == ARG
     assert _score(_keys(), S=-1) == ARG
     assert _score(_keys(), D=0) == ARG
-    assert _score(_keys(), kernel=5) == ARG
+    assert _score(_keys(), kernel=6) == ARG
     assert _score(_keys(), kernel=-1) == ARG
     assert _score(_keys(), S=1 << 24, kernel=2) == UNSUP
     assert _score(_keys(layout=1, bits=4), C=16) == UNSUP
