@@ -116,7 +116,7 @@ const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int 
     if (kernel == TQ_KERNEL_VALU)
         return layout == TQ_UNPACKED ? "valu_unpacked" : bits == 2 ? "valu_packed2" : "valu_packed3";
     if (is_mfma(kernel))
-        return mfma_ok(layout, bits, C, B, S, D, kernel) ? tq::score_mfma_name(layout, b, C, B, D, mfma_variant(kernel))
+        return mfma_ok(layout, bits, C, B, S, D, kernel) ? tq::score_mfma_name(layout, b, C, P, B, S, D, mfma_variant(kernel))
                                                          : nullptr;
     return nullptr;
 }

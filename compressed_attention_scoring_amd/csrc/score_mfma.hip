@@ -441,6 +441,7 @@ __device__ __forceinline__ void key_operands(const TileCodes<NI, NS>& c, int j, 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 constexpr int kValuPerMfma = 7;
 
 // Segment m (0 or 1) of a key: coordinates [m*D/2, (m+1)*D/2).
@@ -583,51 +584,50 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 
     const uint8_t* my_ops = ops + lane * 16;
 
-    while (tile < ntiles) {
-        const int next = tile + stride;
-        TileCodes<NI, NS> nxt;
-        {   // prefetch the next tile while this one is computed (clamped and
-            // unconditional, like the first load)
-            const int s = min(min(next, ntiles - 1) * kTileKeys + col, S - 1);
-            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma, key0 + s, g);
-        }
-
+    // One tile: the key-side operands of k-step j + 1 are built while the LDS
+    // reads and MFMAs of step j are in flight, then the scores are scaled and
+    // stored (the same pipeline as score_qs_kernel, with the query operands read
+    // from LDS).
+    auto tile_scores = [&](const TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
         f32x16 accM[MT], accR[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) { accM[mt][v] = 0.f; accR[mt][v] = 0.f; }
         }
-
+        Op8 chi[2], clo[2], sg[2];
+        key_operands<LAYOUT, BITS, NI, NS>(c, 0, tab_hi, tab_lo, chi[0], clo[0], sg[0]);
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
-            uint32_t x0, x1;
-            F::template selectors<NI>(cur.iw, j, x0, x1);
-            Op8 chi, clo, sg;
-            lut4(x0, tab_hi, chi.u[0], chi.u[1]);
-            lut4(x1, tab_hi, chi.u[2], chi.u[3]);
-            lut4(x0, tab_lo, clo.u[0], clo.u[1]);
-            lut4(x1, tab_lo, clo.u[2], clo.u[3]);
-            F::template signs<NS>(cur.sw, j, sg.u);
+            const int u = j & 1;
+            Op8 ahi[MT], alo[MT], thi[MT], tlo[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const uint8_t* base = my_ops + ((mt * KS + j) * 4) * BLOCK;
-                Op8 ahi, alo, thi, tlo;
-                *reinterpret_cast<uint4*>(ahi.u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
-                *reinterpret_cast<uint4*>(alo.u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
-                *reinterpret_cast<uint4*>(thi.u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
-                *reinterpret_cast<uint4*>(tlo.u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
-                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi.h, chi.h, accM[mt], 0, 0, 0);
-                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi.h, sg.h, accR[mt], 0, 0, 0);
-                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo.h, chi.h, accM[mt], 0, 0, 0);
-                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo.h, sg.h, accR[mt], 0, 0, 0);
-                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi.h, clo.h, accM[mt], 0, 0, 0);
+                *reinterpret_cast<uint4*>(ahi[mt].u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
+                *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
+                *reinterpret_cast<uint4*>(thi[mt].u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
+                *reinterpret_cast<uint4*>(tlo[mt].u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
             }
-            // keep each k-step's operands live only for that step
+            if (j + 1 < KS) key_operands<LAYOUT, BITS, NI, NS>(c, j + 1, tab_hi, tab_lo, chi[u ^ 1], clo[u ^ 1], sg[u ^ 1]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, chi[u].h, accM[mt], 0, 0, 0);
+                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[mt].h, sg[u].h, accR[mt], 0, 0, 0);
+                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[mt].h, chi[u].h, accM[mt], 0, 0, 0);
+                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[mt].h, sg[u].h, accR[mt], 0, 0, 0);
+                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, clo[u].h, accM[mt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * MT, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+#pragma unroll
+            for (int i = 0; i < 5 * MT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, MT == 1 ? 5 : 1, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-
-        const uint32_t lo = lane_offset(tile * kTileKeys + col, S, g);
+        const uint32_t lo = lane_offset(t * kTileKeys + col, S, g);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const __amdgpu_buffer_rsrc_t out_r =
@@ -635,11 +635,27 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float2 k = rowk[mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3)];
-                store_score(out_r, lo + row_offset(v, S), fmaf(k.y * cur.gam, accR[mt][v], accM[mt][v] * k.x));
+                store_score(out_r, lo + row_offset(v, S), fmaf(k.y * c.gam, accR[mt][v], accM[mt][v] * k.x));
             }
         }
-        cur = nxt;
-        tile = next;
+    };
+
+    // Two code buffers in turn, as in score_qs_kernel. Wavefronts without a tile
+    // took part in the prologue (it ends in a barrier) and leave here.
+    if (tile < ntiles) {
+        TileCodes<NI, NS> nxt;
+        while (true) {
+            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma,
+                                       key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+            tile_scores(cur, tile);
+            tile += stride;
+            if (tile >= ntiles) break;
+            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma,
+                                       key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+            tile_scores(nxt, tile);
+            tile += stride;
+            if (tile >= ntiles) break;
+        }
     }
 }
 
@@ -1012,7 +1028,10 @@ hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* 
     const int tpg = kWaves;
     const int lds = (D / 16) * 4 * 1024 * MT + MT * 32 * 8;
     int resident = (160 * 1024) / lds;                // workgroups a CU can hold by LDS
-    if (resident > 8) resident = 8;
+    // Two per CU at most: each workgroup builds the query operands once, so more,
+    // shorter-lived workgroups repeat that work (measured: the packed workload runs
+    // faster with 384-768 workgroups than with 1024).
+    if (resident > 2) resident = 2;
     if (resident < 1) resident = 1;
     const int64_t target = 256LL * resident;           // 256 compute units
     int64_t gx = (ntiles + tpg - 1) / tpg;
@@ -1171,11 +1190,13 @@ bool small_supported(int layout, int bits, int C, int D) {
 // 32-query tile (B <= 32) the workgroup-shared LDS staging wins (its one-time
 // operand build is split over 256 threads); with more query tiles the
 // register-resident operands win (no LDS traffic in the main loop).
-int pick_variant(int layout, int bits, int C, int B, int D) {
-    // one group of four queries: 12 16x16 MFMAs per 16 keys against 40 32x32 ones
-    // per 32 keys padded; with two groups the key decoding doubles and the
-    // padded 32x32 tile measured faster
-    if (B <= 4 && small_supported(layout, bits, C, D)) return kMfmaSmall;
+int pick_variant(int layout, int bits, int C, int B, int64_t keys, int D) {
+    // One group of four queries: 12 16x16 MFMAs per 16 keys against 40 32x32
+    // ones per 32 keys padded. Each wavefront builds its own query operands, so
+    // this pays once wavefronts see many tiles (measured: GQA's 4.2 M keys run
+    // 1.6x faster, one problem of 32 K keys runs slower). With two groups of
+    // four the key decoding doubles and the padded 32x32 tile measured faster.
+    if (B <= 4 && keys >= (int64_t(1) << 20) && small_supported(layout, bits, C, D)) return kMfmaSmall;
     if (B > 32 && reg_supported(layout, bits, C, D)) return kMfmaReg;
     return kMfmaLds;
 }
@@ -1191,9 +1212,9 @@ bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant
     return false;
 }
 
-const char* score_mfma_name(int layout, int bits, int C, int B, int D, int variant) {
+const char* score_mfma_name(int layout, int bits, int C, int P, int B, int S, int D, int variant) {
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return nullptr;
-    if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, D);
+    if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
     if (variant == kMfmaReg) return layout == 0 ? "mfma32reg_unpacked" : bits == 2 ? "mfma32reg_packed2" : "mfma32reg_packed3";
     if (variant == kMfmaSmall) return layout == 0 ? "mfma16_unpacked" : bits == 2 ? "mfma16_packed2" : "mfma16_packed3";
     const int mt = mt_for(B, D);
@@ -1207,7 +1228,7 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              float* scores, int P, int B, int S, int D, int variant,
                              hipStream_t stream) {
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return hipErrorInvalidValue;
-    if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, D);
+    if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
     if (variant == kMfmaSmall) {
         if (layout == 0) return launch_small_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
         if (bits == 2) return launch_small_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);

@@ -43,7 +43,7 @@ enum MfmaVariant { kMfmaAuto = 0, kMfmaLds = 1, kMfmaReg = 2, kMfmaSmall = 3 };
 
 // Returns false if the variant does not cover (layout, bits, C, B, D).
 bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant);
-const char* score_mfma_name(int layout, int bits, int C, int B, int D, int variant);
+const char* score_mfma_name(int layout, int bits, int C, int P, int B, int S, int D, int variant);
 hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              int layout, int bits, const float* codebook, int C,
                              float* scores, int P, int B, int S, int D, int variant,

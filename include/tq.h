@@ -138,7 +138,7 @@ int tq_score(const float* A, const float* T, const tq_keys* keys,
 #define TQ_KERNEL_MFMA16   5  /* matrix cores, 16x16 tiles of four queries times
                                  their four operand rows (the MFMA shapes above
                                  with D in {128, 256}); the automatic choice for
-                                 B <= 4 */
+                                 B <= 4 with P * S >= 2^20 keys */
 
 /*
  * tq_score_with_kernel: tq_score with an explicit kernel family, so that every

@@ -43,8 +43,9 @@ def test_kernel_names_host_only():
     assert n("packed", 2, 4, 1, 32, 131072, 128) == "mfma32_packed2_mt1"
     assert n("packed", 3, 8, 128, 4, 32768, 128) == "mfma16_packed3"
     assert n("packed", 3, 8, 128, 4, 32768, 128, "mfma_lds") == "mfma32_packed3_mt1"
-    assert n("unpacked", 0, 4, 1, 4, 100, 128) == "mfma16_unpacked"
-    assert n("unpacked", 0, 4, 1, 5, 100, 128) == "mfma32_unpacked_mt1"
+    assert n("unpacked", 0, 4, 1, 4, 1 << 20, 128) == "mfma16_unpacked"
+    assert n("unpacked", 0, 4, 1, 4, 32768, 128) == "mfma32_unpacked_mt1"     # few keys: LDS staging
+    assert n("unpacked", 0, 4, 1, 5, 1 << 20, 128) == "mfma32_unpacked_mt1"
     assert n("unpacked", 0, 4, 1, 8, 100, 128, "mfma16") == "mfma16_unpacked"
     assert n("unpacked", 0, 4, 1, 4, 100, 64) == "mfma32_unpacked_mt1"        # 16x16 tiles need D >= 128
     assert n("unpacked", 0, 4, 1, 4, 100, 64, "mfma16") is None
