@@ -39,7 +39,7 @@ _HEADER = os.path.join(os.path.dirname(_PKG), "include", "tq.h")
 TQ_OK = 0
 TQ_UNPACKED = 0
 TQ_PACKED = 1
-KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_lds": 3, "mfma_reg": 4, "mfma16": 5}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_lds": 3, "mfma_reg": 4, "mfma16": 5, "mfma_shared": 6}
 
 
 class _CKeys(ctypes.Structure):

@@ -214,6 +214,12 @@ __device__ __forceinline__ void lut4(uint32_t x, const uint32_t (&tab)[4], uint3
     o1 = perm(hi, lo, 0x07030602u);
 }
 
+// (x & sign bits) | f16 1.0 pair in one v_bitop3_b32 (truth table 0xEA is
+// (S0 & S1) | S2): the sign bits of x become +-1.0 in both f16 halves.
+__device__ __forceinline__ uint32_t signs_of(uint32_t x) {
+    return __builtin_amdgcn_bitop3_b32(x, kSignBits, kOneOne, 0xEA);
+}
+
 template <int LAYOUT, int BITS>
 struct Fmt;
 
@@ -231,10 +237,10 @@ struct Fmt<0, 0> {   // unpacked: one byte per index and per sign
     template <int NS>
     __device__ static __forceinline__ void signs(const uint32_t (&s)[NS], int j, uint32_t (&o)[4]) {
         const uint32_t s0 = s[2 * j], s1 = s[2 * j + 1];
-        o[0] = ((s0 << 8) & kSignBits) | kOneOne;   // coordinates 0, 2
-        o[1] = (s0 & kSignBits) | kOneOne;          // coordinates 1, 3
-        o[2] = ((s1 << 8) & kSignBits) | kOneOne;   // coordinates 4, 6
-        o[3] = (s1 & kSignBits) | kOneOne;          // coordinates 5, 7
+        o[0] = signs_of(s0 << 8);   // coordinates 0, 2
+        o[1] = signs_of(s0);        // coordinates 1, 3
+        o[2] = signs_of(s1 << 8);   // coordinates 4, 6
+        o[3] = signs_of(s1);        // coordinates 5, 7
     }
 };
 
@@ -244,7 +250,7 @@ __device__ __forceinline__ void packed_signs(const uint32_t (&s)[NS], int j, uin
     const uint32_t nv = ~s[j / 4];
     const int k0 = 4 * (j % 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = ((nv << (15 - (k0 + i))) & kSignBits) | kOneOne;
+    for (int i = 0; i < 4; ++i) o[i] = signs_of(nv << (15 - (k0 + i)));
 }
 
 template <>
@@ -835,6 +841,180 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Shared-decode variant (B > 96): the four wavefronts of a workgroup hold four
+// different 32-query tiles in registers (as in score_qs_kernel) and walk the
+// same key tiles. Each key tile is unpacked once per workgroup: wavefront w
+// builds the key-side operands of k-steps [w KS/4, (w+1) KS/4) into one of two
+// LDS buffers while the MFMAs of the previous tile read the other, with one
+// workgroup barrier per tile. This removes the fourfold key decoding of the
+// register variant, whose main loop was bound by vector-ALU issue.
+// ---------------------------------------------------------------------------
+template <int LAYOUT, int BITS, int D>
+struct SharedLds {
+    static constexpr int KS = D / 16;
+    static constexpr int BLOCK = 64 * 16;                       // one operand: 64 lanes x 16 bytes
+    static constexpr int BUF = KS * 3 * BLOCK;                  // chi, clo, sg of every k-step
+};
+
+template <int LAYOUT, int BITS, int D, int W>
+__device__ __forceinline__ void decode_share(const TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
+                                                         Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
+                                             const uint32_t (&tab_hi)[4], const uint32_t (&tab_lo)[4],
+                                             uint8_t* buf, int lane) {
+    using F = Fmt<LAYOUT, BITS>;
+    constexpr int NI = F::template idx_dw<D>(), NS = F::template sign_dw<D>();
+    constexpr int KS = D / 16, JW = KS / kWaves, BLOCK = SharedLds<LAYOUT, BITS, D>::BLOCK;
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+        const int j = W * JW + jj;
+        Op8 chi, clo, sg;
+        key_operands<LAYOUT, BITS, NI, NS>(c, j, tab_hi, tab_lo, chi, clo, sg);
+        uint8_t* base = buf + (j * 3) * BLOCK + lane * 16;
+        *reinterpret_cast<uint4*>(base + 0 * BLOCK) = *reinterpret_cast<const uint4*>(chi.u);
+        *reinterpret_cast<uint4*>(base + 1 * BLOCK) = *reinterpret_cast<const uint4*>(clo.u);
+        *reinterpret_cast<uint4*>(base + 2 * BLOCK) = *reinterpret_cast<const uint4*>(sg.u);
+    }
+}
+
+template <int LAYOUT, int BITS, int D>
+__global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
+    const float* __restrict__ A, const float* __restrict__ T,
+    const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+    const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
+    float* __restrict__ scores, int B, int S, float coef) {
+    using F = Fmt<LAYOUT, BITS>;
+    using L = SharedLds<LAYOUT, BITS, D>;
+    constexpr int HALF = D / 2;
+    constexpr int KS = D / 16;
+    constexpr int NI = F::template idx_dw<D>();
+    constexpr int NS = F::template sign_dw<D>();
+    static_assert(KS % kWaves == 0, "each wavefront unpacks the same number of k-steps");
+
+    __shared__ __attribute__((aligned(16))) uint8_t kops[2 * L::BUF];
+    __shared__ float2 rowk[kWaves][32];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.z;
+    const int b0 = (blockIdx.y * kWaves + wave) * 32;
+    const bool has_q = b0 < B;                 // uniform per wavefront; others only unpack keys
+    const int rows = has_q ? min(32, B - b0) : 0;
+    const int col = lane & 31;
+    const int g = lane >> 5;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    const int64_t key0 = (int64_t)p * S;
+    int tile = blockIdx.x;                     // uniform per workgroup: every barrier is reached by all
+    const int stride = gridDim.x;
+    if (tile >= ntiles) return;
+
+    // query half rows (clamped to a valid row; wavefronts past B never store)
+    const int64_t roff = ((int64_t)p * B + min(b0 + col, B - 1)) * D + g * HALF;
+    float a[HALF], t[HALF];
+#pragma unroll
+    for (int k = 0; k < HALF; k += 4) {
+        const float4 va = *reinterpret_cast<const float4*>(A + roff + k);
+        const float4 vt = *reinterpret_cast<const float4*>(T + roff + k);
+        a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
+        t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+    }
+    TileCodes<NI, NS> c0, c1;
+    asm volatile("" ::: "memory");
+    load_tile<LAYOUT, BITS, D>(c0, idx, sign, gamma, key0 + min(tile * kTileKeys + col, S - 1), g);
+    load_tile<LAYOUT, BITS, D>(c1, idx, sign, gamma,
+                               key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+    asm volatile("" ::: "memory");
+    float sc;
+    uint32_t tab_hi[4], tab_lo[4];
+    codebook_tables(codebook, C, sc, tab_hi, tab_lo);
+
+    float ma = 0.f, mt = 0.f;
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+        ma = fmaxf(ma, fabsf(a[k]));
+        mt = fmaxf(mt, fabsf(t[k]));
+    }
+    ma = fmaxf(ma, __shfl_xor(ma, 32));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float sA = pow2_scale_for(ma);
+    const float sT = pow2_scale_for(mt);
+    if (g == 0) rowk[wave][col] = make_float2(1.f / (sA * sc), coef / sT);
+    Op8 ahi[KS], alo[KS], thi[KS], tlo[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xa = a[mse_dim<LAYOUT, BITS>(j, e)] * sA;
+            const _Float16 ha = (_Float16)xa;
+            ahi[j].h[e] = ha;
+            alo[j].h[e] = (_Float16)(xa - (float)ha);
+            const float xt = t[qjl_dim<LAYOUT>(j, e)] * sT;
+            const _Float16 ht = (_Float16)xt;
+            thi[j].h[e] = ht;
+            tlo[j].h[e] = (_Float16)(xt - (float)ht);
+        }
+    }
+
+    auto decode = [&](const TileCodes<NI, NS>& c, uint8_t* buf) __attribute__((always_inline)) {
+        switch (wave) {
+            case 0: decode_share<LAYOUT, BITS, D, 0>(c, tab_hi, tab_lo, buf, lane); break;
+            case 1: decode_share<LAYOUT, BITS, D, 1>(c, tab_hi, tab_lo, buf, lane); break;
+            case 2: decode_share<LAYOUT, BITS, D, 2>(c, tab_hi, tab_lo, buf, lane); break;
+            default: decode_share<LAYOUT, BITS, D, 3>(c, tab_hi, tab_lo, buf, lane); break;
+        }
+    };
+    decode(c0, kops);
+    __syncthreads();
+
+    // wavefronts past B compute too (no branch around the stores keeps the wait
+    // counts exact); their descriptor covers no rows, so every store is dropped
+    const __amdgpu_buffer_rsrc_t out_r = score_rows(scores + ((int64_t)p * B + (has_q ? b0 : 0)) * S, rows, S);
+    float gam_cur = c0.gam;
+
+    // One tile from LDS buffer `buf`. First the next tile's codes `cn` are
+    // unpacked into the other buffer (its gamma kept for the next step) and `cr`
+    // is refilled two tiles ahead; one barrier ends the step.
+    auto step = [&](int t, uint8_t* buf, uint8_t* other, const TileCodes<NI, NS>& cn, TileCodes<NI, NS>& cr)
+        __attribute__((always_inline)) {
+        if (t + stride < ntiles) decode(cn, other);
+        const float gam_next = cn.gam;
+        load_tile<LAYOUT, BITS, D>(cr, idx, sign, gamma,
+                                   key0 + min(min(t + 2 * stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+        f32x16 accM, accR;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { accM[v] = 0.f; accR[v] = 0.f; }
+        const uint8_t* my = buf + lane * 16;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            Op8 chi, clo, sg;
+            *reinterpret_cast<uint4*>(chi.u) = *reinterpret_cast<const uint4*>(my + (j * 3 + 0) * L::BLOCK);
+            *reinterpret_cast<uint4*>(clo.u) = *reinterpret_cast<const uint4*>(my + (j * 3 + 1) * L::BLOCK);
+            *reinterpret_cast<uint4*>(sg.u) = *reinterpret_cast<const uint4*>(my + (j * 3 + 2) * L::BLOCK);
+            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, chi.h, accM, 0, 0, 0);
+            accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, sg.h, accR, 0, 0, 0);
+            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, chi.h, accM, 0, 0, 0);
+            accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[j].h, sg.h, accR, 0, 0, 0);
+            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, clo.h, accM, 0, 0, 0);
+        }
+        const uint32_t lo = lane_offset(t * kTileKeys + col, S, g);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float2 k = rowk[wave][8 * (v >> 2) + 4 * g + (v & 3)];
+            store_score(out_r, lo + row_offset(v, S), fmaf(k.y * gam_cur, accR[v], accM[v] * k.x));
+        }
+        gam_cur = gam_next;
+        __syncthreads();
+    };
+    while (true) {
+        step(tile, kops, kops + L::BUF, c1, c0);
+        tile += stride;
+        if (tile >= ntiles) break;
+        step(tile, kops + L::BUF, kops, c0, c1);
+        tile += stride;
+        if (tile >= ntiles) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Small-batch variant (a few queries per problem): v_mfma_f32_16x16x32_f16 with the 16 keys of a
 // tile as columns and, as the 16 rows, four queries times four operand types:
 // row 4 b + type holds A_hi, A_lo, T_hi or T_lo of query b. A 32-wide
@@ -1121,6 +1301,32 @@ hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, con
     return hipErrorInvalidValue;
 }
 
+// Shared-decode launch: workgroup rows are groups of four 32-query tiles; two
+// workgroups per CU are resident (registers), so 512 workgroups fill the chip.
+template <int LAYOUT, int BITS, int D>
+hipError_t launch_shared_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
+                           float* scores, int P, int B, int S, hipStream_t stream) {
+    const int groups_y = (B + 127) / 128;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    int64_t gx = ntiles;
+    int64_t cap = 512 / ((int64_t)groups_y * P);
+    if (cap < 1) cap = 1;
+    if (gx > cap) gx = cap;
+    const float coef = (float)(kSqrtHalfPi / (double)D);
+    hipLaunchKernelGGL((score_shared_kernel<LAYOUT, BITS, D>), dim3((unsigned)gx, groups_y, P),
+                       dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
+                       scores, B, S, coef);
+    return hipGetLastError();
+}
+
+template <int LAYOUT, int BITS>
+hipError_t launch_shared_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
+                                int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
+    if (D == 64) return launch_shared_d<LAYOUT, BITS, 64>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 128) return launch_shared_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
+    return hipErrorInvalidValue;
+}
+
 template <int LAYOUT, int BITS>
 hipError_t launch_qs_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                             int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
@@ -1182,6 +1388,10 @@ bool reg_supported(int layout, int bits, int C, int D) {
     return lds_supported(layout, bits, C, D) && D <= 128;   // D = 256 would need 256 operand registers
 }
 
+bool shared_supported(int layout, int bits, int C, int D) {
+    return lds_supported(layout, bits, C, D) && (D == 64 || D == 128);   // k-steps split over 4 wavefronts
+}
+
 bool small_supported(int layout, int bits, int C, int D) {
     return lds_supported(layout, bits, C, D) && (D == 128 || D == 256);   // a lane owns D/4 >= 32 coordinates
 }
@@ -1197,6 +1407,10 @@ int pick_variant(int layout, int bits, int C, int B, int64_t keys, int D) {
     // 1.6x faster, one problem of 32 K keys runs slower). With two groups of
     // four the key decoding doubles and the padded 32x32 tile measured faster.
     if (B <= 4 && keys >= (int64_t(1) << 20) && small_supported(layout, bits, C, D)) return kMfmaSmall;
+    // Four or more query tiles: the shared-decode variant unpacks each key tile
+    // once for all four (long workload 51.3 -> 48.3 us against the register
+    // variant); with three, one of its four wavefronts would idle.
+    if (B > 96 && shared_supported(layout, bits, C, D)) return kMfmaShared;
     if (B > 32 && reg_supported(layout, bits, C, D)) return kMfmaReg;
     return kMfmaLds;
 }
@@ -1209,6 +1423,7 @@ bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant
     if (variant == kMfmaLds) return lds_supported(layout, bits, C, D);
     if (variant == kMfmaReg) return reg_supported(layout, bits, C, D);
     if (variant == kMfmaSmall) return small_supported(layout, bits, C, D);
+    if (variant == kMfmaShared) return shared_supported(layout, bits, C, D);
     return false;
 }
 
@@ -1217,6 +1432,7 @@ const char* score_mfma_name(int layout, int bits, int C, int P, int B, int S, in
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
     if (variant == kMfmaReg) return layout == 0 ? "mfma32reg_unpacked" : bits == 2 ? "mfma32reg_packed2" : "mfma32reg_packed3";
     if (variant == kMfmaSmall) return layout == 0 ? "mfma16_unpacked" : bits == 2 ? "mfma16_packed2" : "mfma16_packed3";
+    if (variant == kMfmaShared) return layout == 0 ? "mfma32shared_unpacked" : bits == 2 ? "mfma32shared_packed2" : "mfma32shared_packed3";
     const int mt = mt_for(B, D);
     if (layout == 0) return mt == 4 ? "mfma32_unpacked_mt4" : mt == 2 ? "mfma32_unpacked_mt2" : "mfma32_unpacked_mt1";
     if (bits == 2) return mt == 4 ? "mfma32_packed2_mt4" : mt == 2 ? "mfma32_packed2_mt2" : "mfma32_packed2_mt1";
@@ -1229,6 +1445,11 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              hipStream_t stream) {
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return hipErrorInvalidValue;
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
+    if (variant == kMfmaShared) {
+        if (layout == 0) return launch_shared_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        if (bits == 2) return launch_shared_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        return launch_shared_layout<1, 3>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+    }
     if (variant == kMfmaSmall) {
         if (layout == 0) return launch_small_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
         if (bits == 2) return launch_small_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);

@@ -139,6 +139,11 @@ int tq_score(const float* A, const float* T, const tq_keys* keys,
                                  their four operand rows (the MFMA shapes above
                                  with D in {128, 256}); the automatic choice for
                                  B <= 4 with P * S >= 2^20 keys */
+#define TQ_KERNEL_MFMA_SHARED 6  /* matrix cores, four query tiles per workgroup in
+                                    registers sharing one unpacking of each key
+                                    tile through LDS (the MFMA shapes above with
+                                    D in {64, 128}); the automatic choice for
+                                    B > 96 */
 
 /*
  * tq_score_with_kernel: tq_score with an explicit kernel family, so that every

@@ -49,7 +49,10 @@ def test_kernel_names_host_only():
     assert n("unpacked", 0, 4, 1, 8, 100, 128, "mfma16") == "mfma16_unpacked"
     assert n("unpacked", 0, 4, 1, 4, 100, 64) == "mfma32_unpacked_mt1"        # 16x16 tiles need D >= 128
     assert n("unpacked", 0, 4, 1, 4, 100, 64, "mfma16") is None
-    assert n("packed", 3, 8, 1, 128, 262144, 128) == "mfma32reg_packed3"
+    assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_shared") == "mfma32shared_packed3"
+    assert n("packed", 3, 8, 1, 128, 262144, 256, "mfma_shared") is None
+    assert n("packed", 3, 8, 1, 128, 262144, 128) == "mfma32shared_packed3"
+    assert n("packed", 3, 8, 1, 96, 262144, 128) == "mfma32reg_packed3"
     assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_lds") == "mfma32_packed3_mt4"
     assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_reg") == "mfma32reg_packed3"
     assert n("unpacked", 0, 4, 1, 32, 32768, 128, "mfma_reg") == "mfma32reg_unpacked"
@@ -84,7 +87,7 @@ def test_score_rejects_bad_arguments_before_launch():
     assert _score(_keys(layout=5)) == ARG
     assert _score(_keys(), S=-1) == ARG
     assert _score(_keys(), D=0) == ARG
-    assert _score(_keys(), kernel=6) == ARG
+    assert _score(_keys(), kernel=7) == ARG
     assert _score(_keys(), kernel=-1) == ARG
     assert _score(_keys(), S=1 << 24, kernel=2) == UNSUP
     assert _score(_keys(layout=1, bits=4), C=16) == UNSUP

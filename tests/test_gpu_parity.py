@@ -88,7 +88,7 @@ for layout, bits, C in (("unpacked", 0, 4), ("unpacked", 0, 8), ("packed", 2, 4)
             SCORE_CASES.append((layout, bits, C, D, B, S))
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg", "mfma16"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
 @pytest.mark.parametrize("layout,bits,C,D,B,S", SCORE_CASES)
 def test_score_random_codes(kernel, layout, bits, C, D, B, S):
     if tq.tq_score_kernel_name(layout, bits, C, 2, B, S, D, kernel) is None:
@@ -120,7 +120,7 @@ def test_score_valu_odd_dims(D):
     assert rel_err(got, oracle_scores_transformed(A, T, idx_u, sign_u, gamma_k, cb)) <= SCORE_TOL
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg", "mfma16"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
 @pytest.mark.parametrize("B", [3, 32, 100])
 @pytest.mark.parametrize("scale", [1e-6, 1e4, 3e5])
 def test_score_extreme_magnitudes(kernel, B, scale):
