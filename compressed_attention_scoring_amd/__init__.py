@@ -1,13 +1,14 @@
 """Compressed-key attention scoring on MI355X (gfx950): Python binding.
 
 Thin ctypes layer over the C ABI in ``include/tq.h`` (library ``libtq.so``,
-built in-tree by ``python -m compressed_attention_scoring_amd.build``). The
+built in-tree by ``python compressed_attention_scoring_amd/build.py``). The
 functions keep the C names:
 
     tq_query_transform(q, Pi, S_mat)           -> (A, T)
     tq_score(A, T, keys, codebook)             -> scores
     tq_score_with_kernel(A, T, keys, codebook, kernel)
     tq_decode_debug(keys, D)                   -> (idx, sign, gamma)
+    tq_compress_keys(keys, Pi, S_mat, codebook, layout, bits) -> Keys
     tq_score_kernel_name(layout, bits, C, P, B, S, D, kernel)
 
 Only argument marshalling happens here: shapes, dtypes, contiguity and device
@@ -28,7 +29,7 @@ import torch
 
 __all__ = [
     "Keys", "TqError", "tq_query_transform", "tq_score", "tq_score_with_kernel",
-    "tq_decode_debug", "tq_score_kernel_name", "tq_status_string", "library_path",
+    "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
     "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
 ]
 
@@ -52,10 +53,20 @@ class _CKeys(ctypes.Structure):
     ]
 
 
+class _CKeysOut(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("idx", ctypes.c_void_p),
+        ("sign", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p),
+    ]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is not built; run `python -m compressed_attention_scoring_amd.build` "
+            f"{_LIB_PATH} is not built; run `python compressed_attention_scoring_amd/build.py` "
             "(needs hipcc) before using the library")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int
@@ -70,6 +81,8 @@ def _load():
     lib.tq_score_kernel_name.restype = ctypes.c_char_p
     lib.tq_decode_debug.argtypes = [ctypes.POINTER(_CKeys), vp, vp, vp, i32, i32, i32, vp]
     lib.tq_decode_debug.restype = i32
+    lib.tq_compress_keys.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(_CKeysOut), i32, i32, i32, i32, vp]
+    lib.tq_compress_keys.restype = i32
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     return lib
@@ -249,3 +262,39 @@ def tq_decode_debug(keys: Keys, D: int, stream=None):
     _check(_lib.tq_decode_debug(ctypes.byref(ck), _ptr(idx), _ptr(sign), _ptr(gamma),
                                 P, S, D, st), "tq_decode_debug")
     return idx, sign, gamma
+
+
+def tq_compress_keys(keys: torch.Tensor, Pi: torch.Tensor, S_mat: torch.Tensor, codebook: torch.Tensor,
+                     layout: str = "packed", bits: int = 3, stream=None) -> Keys:
+    """Compress float32 keys [P,S,D] (or [S,D]) with head p % H's Pi and S_mat into a new Keys."""
+    k3 = _as3(_gpu(keys, "keys", torch.float32))
+    Pi3 = _as3(_gpu(Pi, "Pi", torch.float32))
+    S3 = _as3(_gpu(S_mat, "S_mat", torch.float32))
+    _gpu(codebook, "codebook", torch.float32)
+    P, S, D = k3.shape
+    H = Pi3.shape[0]
+    if Pi3.shape != (H, D, D) or S3.shape != (H, D, D):
+        raise ValueError(f"Pi and S_mat must be [H, {D}, {D}]")
+    dev = keys.device
+    if layout == "unpacked":
+        lay, b = TQ_UNPACKED, 0
+        idx = torch.empty((P, S, D), dtype=torch.uint8, device=dev)
+        sign = torch.empty((P, S, D), dtype=torch.int8, device=dev)
+        gamma = torch.empty((P, S), dtype=torch.float32, device=dev)
+    elif layout == "packed":
+        lay, b = TQ_PACKED, int(bits)
+        if b not in (2, 3) or D % 8:
+            raise ValueError("packed keys need bits in (2, 3) and D % 8 == 0")
+        idx = torch.empty((P, S, D * b // 8), dtype=torch.uint8, device=dev)
+        sign = torch.empty((P, S, D // 8), dtype=torch.uint8, device=dev)
+        gamma = torch.empty((P, S), dtype=torch.float16, device=dev)
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    out = _CKeysOut(lay, b, idx.data_ptr(), sign.data_ptr(), gamma.data_ptr())
+    st = _stream(dev, stream)
+    _check(_lib.tq_compress_keys(_ptr(k3), _ptr(Pi3), _ptr(S3), _ptr(codebook), codebook.numel(),
+                                 ctypes.byref(out), P, H, S, D, st), "tq_compress_keys")
+    squeeze = keys.dim() == 2
+    if squeeze:
+        idx, sign, gamma = idx[0], sign[0], gamma[0]
+    return Keys(layout, idx, sign, gamma, bits=b)

@@ -1,6 +1,9 @@
 """Build the HIP library (libtq.so) for gfx950, in-tree.
 
-    python -m compressed_attention_scoring_amd.build
+    python compressed_attention_scoring_amd/build.py
+
+(run as a file: importing the package loads libtq.so, which must not be
+needed to build it).
 
 Each .hip source is compiled to an object with hipcc, then linked into
 ``compressed_attention_scoring_amd/libtq.so``. Packed-FP32 instructions are
@@ -23,7 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["abi.hip", "query_transform.hip", "score_valu.hip", "score_mfma.hip", "decode.hip"]
+SOURCES = ["abi.hip", "query_transform.hip", "score_valu.hip", "score_mfma.hip", "decode.hip", "compress.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

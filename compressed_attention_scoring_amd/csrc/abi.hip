@@ -155,6 +155,26 @@ int tq_score(const float* A, const float* T, const tq_keys* keys, const float* c
     return tq_score_with_kernel(A, T, keys, codebook, C, scores, P, B, S, D, TQ_KERNEL_AUTO, stream);
 }
 
+int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat, const float* codebook, int C,
+                     const tq_keys_out* out, int P, int H, int S, int D, void* stream) {
+    if (!out || P < 0 || S < 0 || H <= 0 || D <= 0) return TQ_ERR_ARG;
+    if (out->layout != TQ_UNPACKED && out->layout != TQ_PACKED) return TQ_ERR_ARG;
+    if (P % H != 0) return TQ_ERR_ARG;
+    const int bits = out->layout == TQ_PACKED ? out->bits : 0;
+    if (out->layout == TQ_PACKED && ((bits != 2 && bits != 3) || C != (1 << bits))) return TQ_ERR_UNSUPPORTED;
+    if (!tq::compress_supported(out->layout, bits, C, D)) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || S == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!keys || !Pi || !S_mat || !codebook || !out->idx || !out->sign || !out->gamma) return TQ_ERR_ARG;
+    if (P > 65535 || !fits(P, S, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(keys) || !aligned16(Pi) || !aligned16(S_mat) || !aligned16(codebook) || !aligned16(out->idx) ||
+        !aligned16(out->sign) || !aligned16(out->gamma))
+        return TQ_ERR_ALIGN;
+    const tq::KeyOut ko{static_cast<uint8_t*>(out->idx), static_cast<uint8_t*>(out->sign), out->gamma};
+    const hipError_t e = tq::launch_compress(keys, Pi, S_mat, codebook, C, ko, out->layout, bits, P, H, S, D,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                     int P, int S, int D, void* stream) {
     if (P < 0 || S < 0) return TQ_ERR_ARG;

@@ -49,6 +49,17 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              float* scores, int P, int B, int S, int D, int variant,
                              hipStream_t stream);
 
+// Compressor outputs (device pointers; layout and sizes as in KeyStreams).
+struct KeyOut {
+    uint8_t* idx;
+    uint8_t* sign;
+    void* gamma;
+};
+bool compress_supported(int layout, int bits, int C, int D);
+hipError_t launch_compress(const float* keys, const float* Pi, const float* S_mat, const float* codebook,
+                           int C, KeyOut out, int layout, int bits, int P, int H, int S, int D,
+                           hipStream_t stream);
+
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                          int P, int S, int D, hipStream_t stream);

@@ -173,6 +173,45 @@ const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int 
 int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out,
                     float* gamma_out, int P, int S, int D, void* stream);
 
+/*
+ * Output descriptor of tq_compress_keys: the same layouts as tq_keys, with
+ * writable device pointers.
+ */
+typedef struct tq_keys_out {
+    int32_t layout;   /* TQ_UNPACKED or TQ_PACKED */
+    int32_t bits;     /* packed: 2 or 3 */
+    void* idx;
+    void* sign;
+    void* gamma;
+} tq_keys_out;
+
+/*
+ * tq_compress_keys: compress keys into either layout above (the inner-product
+ * quantizer of "TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits",
+ * section 3, with the residual norm of "TurboQuant Attention in CUDA",
+ * section "The keys arrived in pieces"). For each key k of problem p, with
+ * head h = p % H:
+ *   y = Pi_h k;  idx_d = number of codebook midpoints strictly below y_d
+ *   (a value on a midpoint takes the lower index);  r = k - Pi_h^T c[idx];
+ *   gamma = ||r||;  sign_d = +1 if (S_h r)_d >= 0 else -1.
+ * Keys are compressed as given: the method assumes unit keys (normalise first).
+ *
+ *   keys      float32 [P, S, D]
+ *   Pi, S_mat float32 [H, D, D]   (the matrices tq_query_transform takes)
+ *   codebook  float32 [C]         sorted ascending, 2 <= C <= 16; packed: C == 2^bits
+ *   out       host pointer to the descriptor; its device buffers are written
+ *
+ * Arithmetic is float64, so indices and signs equal those of a float64
+ * reference except for values within rounding distance of a midpoint or of a
+ * zero projection; gamma is rounded once to float32 (unpacked) or binary16
+ * (packed). D in {64, 128}. TQ_ERR_ARG for bad pointers or sizes (as above,
+ * P % H != 0), TQ_ERR_UNSUPPORTED for other D or C, TQ_ERR_ALIGN for a buffer
+ * that is not 16-byte aligned. Empty calls (P or S == 0) return TQ_OK.
+ */
+int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat,
+                     const float* codebook, int C, const tq_keys_out* out,
+                     int P, int H, int S, int D, void* stream);
+
 /* tq_status_string: static description of a status code. */
 const char* tq_status_string(int status);
 

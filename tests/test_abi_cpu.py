@@ -11,7 +11,7 @@ import compressed_attention_scoring_amd as tq
 
 EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
-    "tq_decode_debug", "tq_status_string",
+    "tq_decode_debug", "tq_compress_keys", "tq_status_string",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -133,3 +133,21 @@ def test_binding_refuses_cpu_tensors():
     Pi = torch.eye(8)
     with pytest.raises(ValueError, match="GPU"):
         tq.tq_query_transform(q, Pi, Pi)
+
+
+def test_compress_rejects_bad_arguments():
+    f = tq._lib.tq_compress_keys
+    out = lambda layout=0, bits=0, idx=16, sign=16, gamma=16: ctypes.byref(tq._CKeysOut(layout, bits, idx, sign, gamma))
+    assert f(16, 16, 16, 16, 4, None, 1, 1, 8, 128, None) == ARG
+    assert f(16, 16, 16, 16, 4, out(layout=7), 1, 1, 8, 128, None) == ARG
+    assert f(16, 16, 16, 16, 4, out(), 3, 2, 8, 128, None) == ARG           # P % H != 0
+    assert f(16, 16, 16, 16, 4, out(), 1, 0, 8, 128, None) == ARG
+    assert f(None, 16, 16, 16, 4, out(), 1, 1, 8, 128, None) == ARG
+    assert f(16, 16, 16, 16, 4, out(idx=None), 1, 1, 8, 128, None) == ARG
+    assert f(16, 16, 16, 16, 4, out(), 1, 1, 8, 96, None) == UNSUP          # D not in {64, 128}
+    assert f(16, 16, 16, 16, 32, out(), 1, 1, 8, 128, None) == UNSUP        # C > 16
+    assert f(16, 16, 16, 16, 4, out(layout=1, bits=3), 1, 1, 8, 128, None) == UNSUP   # C != 2^bits
+    assert f(20, 16, 16, 16, 4, out(), 1, 1, 8, 128, None) == ALIGN
+    assert f(16, 16, 16, 16, 4, out(gamma=24), 1, 1, 8, 128, None) == ALIGN
+    assert f(None, None, None, None, 4, out(idx=None, sign=None, gamma=None), 1, 1, 0, 128, None) == OK
+    assert f(None, None, None, None, 4, out(idx=None, sign=None, gamma=None), 0, 1, 8, 128, None) == OK
