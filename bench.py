@@ -21,6 +21,7 @@ Prints ONE JSON line. ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "query-key scores/sec + achieved HBM GB/s, B=32 S=32768 D=128 3-bit keys"
 HBM_PEAK_GBS = 8000.0
+FP64_MATRIX_PEAK_TFLOPS = 78.6
 RING_BYTES = 512 * 1024 * 1024
 
 
@@ -49,7 +51,10 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     help="decode (default, the quoted configuration); others for profiling")
     ap.add_argument("--kernel", default="auto",
-                    choices=["auto", "valu", "mfma"])
+                    choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
+    ap.add_argument("--path", default="score", choices=["score", "compress"],
+                    help="score (default): the scoring hot path; compress: the key compressor "
+                         "(tq_compress_keys) on the workload's key set")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -240,6 +245,106 @@ def cpu_baseline(w, host, target_s):
     }
 
 
+def bench_compress(args, w, device) -> dict:
+    """Time tq_compress_keys on the workload's P*S keys (float64 arithmetic,
+    three D x D products per key on the fp64 matrix cores)."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+    from oracle.codebook import codebook_fp32
+
+    Pi, S_mat = synth.head_matrices(w.seed, w.H, w.D)
+    cb = codebook_fp32(w.D, w.C)
+    one = synth.unit_keys(synth.keys_rng(w.seed, 0), w.S, w.D, w.keys).astype(np.float32)
+    keys_dev = torch.from_numpy(one).to(device).unsqueeze(0).expand(w.P, w.S, w.D).contiguous()
+    shared = [torch.from_numpy(a).to(device) for a in (Pi, S_mat, cb)]
+    per_set = keys_dev.numel() * 4 + w.key_bytes()
+    nsets = max(2, min(32, math.ceil(RING_BYTES / per_set)))
+    ring = [keys_dev.clone() for _ in range(nsets)]
+    bits = w.bits if w.layout == "packed" else 0
+    outs = [tq.tq_compress_keys(k, *shared, w.layout, bits) for k in ring]   # allocates the outputs once
+    torch.cuda.synchronize()
+
+    def launch(i):
+        k, o = ring[i], outs[i]
+        out = tq._CKeysOut(tq.TQ_UNPACKED if w.layout == "unpacked" else tq.TQ_PACKED, bits,
+                           o.idx.data_ptr(), o.sign.data_ptr(), o.gamma.data_ptr())
+        st = torch.cuda.current_stream(device).cuda_stream
+        rc = tq._lib.tq_compress_keys(k.data_ptr(), shared[0].data_ptr(), shared[1].data_ptr(),
+                                      shared[2].data_ptr(), w.C, ctypes.byref(out), w.P, w.H, w.S, w.D, st)
+        if rc != 0:
+            raise tq.TqError(rc, "tq_compress_keys")
+
+    for i in range(args.warmup):
+        launch(i % nsets)
+    torch.cuda.synchronize()
+    steps = args.steps
+    chunks = [nsets] * (steps // nsets) + ([steps % nsets] if steps % nsets else [])
+    graphs = {}
+    for n in sorted(set(chunks)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                launch(i)
+        graphs[n] = g
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for n in chunks:
+        graphs[n].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    nkeys = w.P * w.S
+    flops = 6 * w.D * w.D * nkeys          # y = Pi k, x = Pi^T c, p = S_mat r
+    achieved = flops / (us * 1e-6) / 1e12
+    log(f"compress: {steps} launches, {us:.2f} us per launch ({nkeys} keys), {achieved:.1f} TFLOP/s fp64")
+    out = {
+        "metric": "keys compressed/sec (TurboQuant_prod, float64 arithmetic)",
+        "value": nkeys / (us * 1e-6),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic: seeded unit keys (Gaussian with outlier channels), Haar rotation, Gaussian projection",
+        "config": {"workload": w.name, "path": "compress", "P": w.P, "S": w.S, "D": w.D, "C": w.C,
+                   "layout": w.layout, "bits": w.bits},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP64_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP64_MATRIX_PEAK_TFLOPS, "traffic": None,
+                     "kernel": f"compress_{w.layout}{bits if bits else ''}", "flops_per_launch": flops,
+                     "avg_launch_us": us},
+        "ring_sets": nsets,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import compress as oc
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        k64 = one.astype(np.float64)
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3:
+            t1 = time.perf_counter()
+            oc.quantize_prod_unit(k64, Pi[0], S_mat[0], cb)
+            times.append(time.perf_counter() - t1)
+        med = sorted(times)[len(times) // 2]
+        out["cpu_baseline"] = {"value": w.S / med, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"one problem's {w.S} keys (D={w.D}) compressed by the float64 oracle, "
+                                         f"median of {len(times)} runs ({sum(times):.1f} s total)"}
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -258,6 +363,9 @@ def main() -> int:
         raise SystemExit("bench.py needs a GPU")
     device = torch.device("cuda:0")
     w = synth.workload(args.workload)
+    if args.path == "compress":
+        print(json.dumps(bench_compress(args, w, device)), flush=True)
+        return 0
     kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, args.kernel)
     log(f"workload {w.describe()} kernel {kname}")
     ring, shared, host, per_set = build_ring(w, device, w.seed)
