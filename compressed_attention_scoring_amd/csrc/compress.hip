@@ -62,7 +62,7 @@ struct CompressLds {
     static constexpr int PER_WAVE = 2 * BYTES;
 };
 
-template <int D, int LAYOUT, int BITS>
+template <int D, int LAYOUT, int BITS, int NC>
 __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     const float* __restrict__ keys, const float* __restrict__ Pi, const float* __restrict__ Smat,
     const float* __restrict__ codebook, int C, uint8_t* __restrict__ idx_out, uint8_t* __restrict__ sign_out,
@@ -87,13 +87,6 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     uint8_t* ibuf = lds + wave * L::PER_WAVE;                  // [16][D] indices
     uint8_t* sbuf = ibuf + L::BYTES;                            // [16][D] sign bits (0/1)
 
-    // codebook and its midpoints (sorted codebook, C <= 16)
-    double cb[kMaxCodebook], edge[kMaxCodebook - 1];
-#pragma unroll
-    for (int i = 0; i < kMaxCodebook; ++i) cb[i] = i < C ? (double)codebook[i] : 0.0;
-#pragma unroll
-    for (int i = 0; i + 1 < kMaxCodebook; ++i) edge[i] = 0.5 * (cb[i] + cb[i + 1]);
-
     // ---- 1. y = Pi k: B holds this lane's key at j = 16 kq + 4 q + t
     f64x4 acc[RB];
 #pragma unroll
@@ -113,6 +106,13 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     // ---- 2. indices: acc[rb][v] = y[d = 16 rb + 4 v + q] of key col; the index
     //      is the number of midpoints strictly below y (a value on a midpoint
     //      takes the lower index)
+    // codebook and its midpoints (sorted codebook, C <= NC), built here so they
+    // are not live during the first product
+    double cb[NC], edge[NC - 1];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) cb[i] = i < C ? (double)codebook[i] : 0.0;
+#pragma unroll
+    for (int i = 0; i + 1 < NC; ++i) edge[i] = 0.5 * (cb[i] + cb[i + 1]);
     f64x4 cr[RB];                              // c = codebook[idx], later r
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -120,11 +120,11 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
         for (int v = 0; v < 4; ++v) {
             int n = 0;
 #pragma unroll
-            for (int i = 0; i + 1 < kMaxCodebook; ++i) n += (i + 1 < C && edge[i] < acc[rb][v]) ? 1 : 0;
+            for (int i = 0; i + 1 < NC; ++i) n += (i + 1 < C && edge[i] < acc[rb][v]) ? 1 : 0;
             ibuf[col * D + 16 * rb + 4 * v + q] = (uint8_t)n;
             double c = cb[0];
 #pragma unroll
-            for (int i = 1; i < kMaxCodebook; ++i) c = n == i ? cb[i] : c;
+            for (int i = 1; i < NC; ++i) c = n == i ? cb[i] : c;
             cr[rb][v] = c;
         }
     }
@@ -244,8 +244,13 @@ hipError_t launch_compress_d(const float* keys, const float* Pi, const float* S_
                              int C, KeyOut out, int P, int H, int S, hipStream_t stream) {
     const int per_block = kCompressWaves * kKeysPerWave;
     const dim3 grid((unsigned)((S + per_block - 1) / per_block), (unsigned)P);
-    hipLaunchKernelGGL((compress_kernel<D, LAYOUT, BITS>), grid, dim3(kCompressWaves * 64), 0, stream,
-                       keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, H, S);
+    // codebook registers sized to the codebook: 8 entries cover every packed format
+    if (C <= 8)
+        hipLaunchKernelGGL((compress_kernel<D, LAYOUT, BITS, 8>), grid, dim3(kCompressWaves * 64), 0, stream,
+                           keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, H, S);
+    else
+        hipLaunchKernelGGL((compress_kernel<D, LAYOUT, BITS, kMaxCodebook>), grid, dim3(kCompressWaves * 64), 0,
+                           stream, keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, H, S);
     return hipGetLastError();
 }
 
