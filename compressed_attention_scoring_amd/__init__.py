@@ -9,6 +9,8 @@ functions keep the C names:
     tq_score_with_kernel(A, T, keys, codebook, kernel)
     tq_decode_debug(keys, D)                   -> (idx, sign, gamma)
     tq_compress_keys(keys, Pi, S_mat, codebook, layout, bits) -> Keys
+    tq_attend(scores, values, codebook, Pi_v, scale) -> out
+    tq_attend_workspace_bytes(P, B, S, D)
     tq_score_kernel_name(layout, bits, C, P, B, S, D, kernel)
 
 Only argument marshalling happens here: shapes, dtypes, contiguity and device
@@ -28,7 +30,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "Keys", "TqError", "tq_query_transform", "tq_score", "tq_score_with_kernel",
+    "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform", "tq_score", "tq_score_with_kernel",
     "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
     "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
 ]
@@ -63,6 +65,15 @@ class _CKeysOut(ctypes.Structure):
     ]
 
 
+class _CValues(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("idx", ctypes.c_void_p),
+        ("norm", ctypes.c_void_p),
+    ]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
@@ -83,6 +94,11 @@ def _load():
     lib.tq_decode_debug.restype = i32
     lib.tq_compress_keys.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(_CKeysOut), i32, i32, i32, i32, vp]
     lib.tq_compress_keys.restype = i32
+    lib.tq_attend_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.tq_attend_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq_attend.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp, vp, ctypes.c_size_t,
+                              i32, i32, i32, i32, i32, vp]
+    lib.tq_attend.restype = i32
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     return lib
@@ -99,7 +115,7 @@ def header_functions() -> list[str]:
     """Names of the functions ``include/tq.h`` declares."""
     with open(_HEADER) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
 
 
 class TqError(RuntimeError):
@@ -298,3 +314,80 @@ def tq_compress_keys(keys: torch.Tensor, Pi: torch.Tensor, S_mat: torch.Tensor, 
     if squeeze:
         idx, sign, gamma = idx[0], sign[0], gamma[0]
     return Keys(layout, idx, sign, gamma, bits=b)
+
+
+@dataclass
+class Values:
+    """Compressed values of P problems with S values of D coordinates each
+    (v_s = norm_s * Pi_v^T codebook[idx_s]).
+
+    layout "unpacked": idx uint8 [P,S,D], norm float32 [P,S].
+    layout "packed":   idx uint8 [P,S,D*bits/8] (LSB-first bitstream), norm float16 [P,S]; bits 2 or 3.
+    A leading problem axis may be omitted (P = 1).
+    """
+    layout: str
+    idx: torch.Tensor
+    norm: torch.Tensor
+    bits: int = 0
+
+    def _c(self, D: int):
+        if self.layout == "unpacked":
+            lay, bits, row, ndt = TQ_UNPACKED, 0, D, torch.float32
+        elif self.layout == "packed":
+            lay, bits, ndt = TQ_PACKED, int(self.bits), torch.float16
+            if bits not in (2, 3) or D % 8:
+                raise ValueError("packed values need bits in (2, 3) and D % 8 == 0")
+            row = D * bits // 8
+        else:
+            raise ValueError(f"unknown layout {self.layout!r}")
+        _gpu(self.idx, "values.idx", torch.uint8)
+        _gpu(self.norm, "values.norm", ndt)
+        n = self.norm if self.norm.dim() == 2 else self.norm.unsqueeze(0)
+        P, S = n.shape
+        if self.idx.numel() != P * S * row:
+            raise ValueError(f"value indices do not match norm's [P={P}, S={S}] with D={D}")
+        return _CValues(lay, bits, self.idx.data_ptr(), self.norm.data_ptr()), P, S
+
+
+def tq_attend_workspace_bytes(P: int, B: int, S: int, D: int) -> int:
+    """Workspace bytes tq_attend needs for this shape."""
+    return int(_lib.tq_attend_workspace_bytes(int(P), int(B), int(S), int(D)))
+
+
+def tq_attend(scores: torch.Tensor, values: Values, codebook: torch.Tensor, Pi_v: torch.Tensor,
+              scale: float | None = None, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """softmax(scale * scores) times the dequantized values: out [P,B,D] (or [B,D]).
+
+    scores [P,B,S] or [B,S]; Pi_v [H,D,D] or [D,D]; scale defaults to 1/sqrt(D).
+    workspace: a uint8 GPU tensor of at least tq_attend_workspace_bytes bytes
+    (allocated here when omitted).
+    """
+    squeeze = scores.dim() == 2
+    s3 = _as3(_gpu(scores, "scores", torch.float32))
+    Pv = _as3(_gpu(Pi_v, "Pi_v", torch.float32))
+    _gpu(codebook, "codebook", torch.float32)
+    P, B, S = s3.shape
+    H, D = Pv.shape[0], Pv.shape[-1]
+    if Pv.shape != (H, D, D):
+        raise ValueError("Pi_v must be [H, D, D]")
+    cv, Pk, Sk = values._c(D)
+    if (Pk, Sk) != (P, S):
+        raise ValueError(f"values hold [P={Pk}, S={Sk}], scores [P={P}, S={S}]")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dev = scores.device
+    if out is None:
+        out = torch.empty((P, B, D), dtype=torch.float32, device=dev)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != P * B * D:
+        raise ValueError("out must hold P*B*D floats")
+    need = tq_attend_workspace_bytes(P, B, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _gpu(workspace, "workspace", torch.uint8)
+    st = _stream(dev, stream)
+    _check(_lib.tq_attend(_ptr(s3), ctypes.byref(cv), _ptr(codebook), codebook.numel(), _ptr(Pv),
+                          float(scale), _ptr(out), _ptr(workspace), workspace.numel(), P, H, B, S, D, st),
+           "tq_attend")
+    return out.view(B, D) if squeeze else out.view(P, B, D)

@@ -175,6 +175,35 @@ int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat, con
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
+size_t tq_attend_workspace_bytes(int P, int B, int S, int D) {
+    if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
+    const int64_t n = (int64_t)P * B * tq::attend_chunks(P, B, S) * (D + 2) * (int64_t)sizeof(float);
+    return (size_t)n;
+}
+
+int tq_attend(const float* scores, const tq_values* values, const float* codebook, int C, const float* Pi_v,
+              float scale, float* out, void* workspace, size_t workspace_bytes, int P, int H, int B, int S, int D,
+              void* stream) {
+    if (!values || P < 0 || B < 0 || S < 0 || H <= 0 || D <= 0 || P % H != 0) return TQ_ERR_ARG;
+    if (values->layout != TQ_UNPACKED && values->layout != TQ_PACKED) return TQ_ERR_ARG;
+    const int bits = values->layout == TQ_PACKED ? values->bits : 0;
+    if (values->layout == TQ_PACKED && ((bits != 2 && bits != 3) || C != (1 << bits))) return TQ_ERR_UNSUPPORTED;
+    if (!tq::attend_supported(values->layout, bits, C, D)) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0) return TQ_OK;   // empty call: nothing to launch
+    if (S == 0) return TQ_ERR_ARG;        // softmax over no keys
+    if (!scores || !codebook || !Pi_v || !out || !workspace || !values->idx || !values->norm) return TQ_ERR_ARG;
+    if (P > 65535 || B > 262144 || !fits(P, B, S) || !fits(P, S, D)) return TQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < tq_attend_workspace_bytes(P, B, S, D)) return TQ_ERR_ARG;
+    if (!aligned16(scores) || !aligned16(codebook) || !aligned16(Pi_v) || !aligned16(out) || !aligned16(workspace) ||
+        !aligned16(values->idx) || !aligned16(values->norm))
+        return TQ_ERR_ALIGN;
+    const tq::ValueStreams v{static_cast<const uint8_t*>(values->idx), values->norm};
+    const hipError_t e = tq::launch_attend(scores, v, values->layout, bits, codebook, C, Pi_v, scale, out,
+                                           static_cast<float*>(workspace), P, H, B, S, D,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                     int P, int S, int D, void* stream) {
     if (P < 0 || S < 0) return TQ_ERR_ARG;

@@ -60,6 +60,20 @@ hipError_t launch_compress(const float* keys, const float* Pi, const float* S_ma
                            int C, KeyOut out, int layout, int bits, int P, int H, int S, int D,
                            hipStream_t stream);
 
+// Compressed values: idx as for keys (unpacked bytes or packed bitstreams),
+// norm float [P,S] (unpacked) or _Float16 [P,S] (packed).
+struct ValueStreams {
+    const uint8_t* idx;
+    const void* norm;
+};
+// Key chunks the attention step splits each (problem, 32-query block) into;
+// the workspace holds P * B * chunks * (D + 2) floats.
+int attend_chunks(int P, int B, int S);
+bool attend_supported(int layout, int bits, int C, int D);
+hipError_t launch_attend(const float* scores, ValueStreams v, int layout, int bits, const float* codebook, int C,
+                         const float* Pi_v, float scale, float* out, float* ws, int P, int H, int B, int S, int D,
+                         hipStream_t stream);
+
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                          int P, int S, int D, hipStream_t stream);

@@ -39,6 +39,7 @@
 #ifndef TQ_H
 #define TQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -211,6 +212,63 @@ typedef struct tq_keys_out {
 int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat,
                      const float* codebook, int C, const tq_keys_out* out,
                      int P, int H, int S, int D, void* stream);
+
+/*
+ * Compressed values of P problems, S values each, D coordinates per value:
+ * the MSE quantizer of "TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits"
+ * (section 3, with the norm kept separately as its value cache does in
+ * section 8): v_s = norm[s] * Pi_v^T codebook[idx[s, :]].
+ *
+ * layout == TQ_UNPACKED: idx uint8 [P, S, D] (< C), norm float32 [P, S]; bits ignored.
+ * layout == TQ_PACKED:   idx uint8 [P, S, D*bits/8] as the packed key indices
+ *                        above (LSB-first bitstream per value), norm float16
+ *                        [P, S]; bits 2 or 3, C == 2^bits.
+ */
+typedef struct tq_values {
+    int32_t layout;
+    int32_t bits;
+    const void* idx;
+    const void* norm;
+} tq_values;
+
+/*
+ * tq_attend_workspace_bytes: bytes of the workspace tq_attend needs for this
+ * shape (0 for an empty shape or invalid sizes). Host-only. The size depends
+ * only on (P, B, S, D).
+ */
+size_t tq_attend_workspace_bytes(int P, int B, int S, int D);
+
+/*
+ * tq_attend: decode attention output from raw scores and compressed values
+ * ("TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits", section 8, kernel
+ * view; the online softmax and split over key ranges of "Fitting 4.4x More
+ * Context on Jetson", FAQ). For each problem p (head h = p % H) and query b:
+ *
+ *   w_s    = exp(scale * scores[p,b,s] - max_t scale * scores[p,b,t])
+ *   out[p,b,:] = Pi_v[h]^T ( sum_s w_s norm[s] codebook[idx[s,:]] ) / sum_s w_s
+ *
+ * which equals softmax(scale * scores) times the dequantized values; the sum is
+ * accumulated in the rotated basis and un-rotated once per query.
+ *
+ *   scores     float32 [P, B, S]   e.g. from tq_score; must be finite
+ *   values     compressed values (struct above; host pointer to the struct)
+ *   codebook   float32 [C]         value centroids, 1 <= C <= 8
+ *   Pi_v       float32 [H, D, D]   value rotation of each head, row-major
+ *   scale      softmax temperature (1/sqrt(D) for standard attention)
+ *   out        float32 [P, B, D]
+ *   workspace  device buffer of at least tq_attend_workspace_bytes(P, B, S, D)
+ *              bytes (per-range partial results; contents on return unspecified)
+ *
+ * D in {64, 128}, S >= 1 when B >= 1 (a softmax over no keys is undefined:
+ * TQ_ERR_ARG). Result: fp32, within 1e-4 * (1 + |exact|) of the exact value.
+ * TQ_ERR_ARG for bad pointers/sizes (as above) or a workspace that is too
+ * small; TQ_ERR_UNSUPPORTED for other D, C or formats; TQ_ERR_ALIGN for a
+ * buffer that is not 16-byte aligned. Calls that share a workspace must be
+ * ordered (same stream).
+ */
+int tq_attend(const float* scores, const tq_values* values, const float* codebook, int C,
+              const float* Pi_v, float scale, float* out, void* workspace, size_t workspace_bytes,
+              int P, int H, int B, int S, int D, void* stream);
 
 /* tq_status_string: static description of a status code. */
 const char* tq_status_string(int status);

@@ -11,7 +11,7 @@ import compressed_attention_scoring_amd as tq
 
 EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
-    "tq_decode_debug", "tq_compress_keys", "tq_status_string",
+    "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -151,3 +151,35 @@ def test_compress_rejects_bad_arguments():
     assert f(16, 16, 16, 16, 4, out(gamma=24), 1, 1, 8, 128, None) == ALIGN
     assert f(None, None, None, None, 4, out(idx=None, sign=None, gamma=None), 1, 1, 0, 128, None) == OK
     assert f(None, None, None, None, 4, out(idx=None, sign=None, gamma=None), 0, 1, 8, 128, None) == OK
+
+
+def test_attend_workspace_size():
+    assert tq.tq_attend_workspace_bytes(0, 4, 100, 128) == 0
+    assert tq.tq_attend_workspace_bytes(1, 4, 0, 128) == 0
+    assert tq.tq_attend_workspace_bytes(1, 4, 100, -1) == 0
+    for P, B, S, D in [(1, 32, 32768, 128), (128, 4, 32768, 128), (1, 1, 1, 64), (3, 70, 1000, 64)]:
+        n = tq.tq_attend_workspace_bytes(P, B, S, D)
+        chunks = n // (P * B * (D + 2) * 4)
+        assert n == P * B * chunks * (D + 2) * 4
+        assert 1 <= chunks <= (S + 31) // 32     # each chunk holds at least one 32-key tile
+
+
+def test_attend_rejects_bad_arguments():
+    f = tq._lib.tq_attend
+    ws = 1 << 30
+    vals = lambda layout=0, bits=0, idx=16, norm=16: ctypes.byref(tq._CValues(layout, bits, idx, norm))
+    assert f(16, None, 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ARG
+    assert f(16, vals(layout=5), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ARG
+    assert f(16, vals(), 16, 4, 16, 1.0, 16, 16, ws, 3, 2, 4, 8, 128, None) == ARG     # P % H != 0
+    assert f(16, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 0, 128, None) == ARG     # no keys
+    assert f(None, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ARG
+    assert f(16, vals(norm=None), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ARG
+    assert f(16, vals(), 16, 4, 16, 1.0, 16, 16, 8, 1, 1, 4, 8, 128, None) == ARG       # workspace too small
+    assert f(16, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 96, None) == UNSUP     # D
+    assert f(16, vals(), 16, 16, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == UNSUP   # C > 8
+    assert f(16, vals(layout=1, bits=3), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == UNSUP
+    assert f(16, vals(layout=1, bits=4), 16, 16, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == UNSUP
+    assert f(20, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ALIGN
+    assert f(16, vals(idx=24), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ALIGN
+    assert f(None, vals(idx=None, norm=None), None, 4, None, 1.0, None, None, 0, 1, 1, 0, 8, 128, None) == OK
+    assert f(None, vals(idx=None, norm=None), None, 4, None, 1.0, None, None, 0, 0, 1, 4, 8, 128, None) == OK
