@@ -52,9 +52,10 @@ def parse():
                     help="decode (default, the quoted configuration); others for profiling")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
-    ap.add_argument("--path", default="score", choices=["score", "compress"],
+    ap.add_argument("--path", default="score", choices=["score", "compress", "attend"],
                     help="score (default): the scoring hot path; compress: the key compressor "
-                         "(tq_compress_keys) on the workload's key set")
+                         "(tq_compress_keys) on the workload's key set; attend: softmax and value "
+                         "aggregation (tq_attend) over the workload's scores and values")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -345,6 +346,119 @@ def bench_compress(args, w, device) -> dict:
     return out
 
 
+def attend_bytes(w) -> int:
+    """Bytes tq_attend must move once: fp32 scores, value indices and norms,
+    the value codebook and rotations in, fp32 outputs out."""
+    if w.layout == "unpacked":
+        per_value = w.D + 4
+    else:
+        per_value = w.D * w.bits // 8 + 2
+    return (w.P * w.B * w.S * 4 + w.P * w.S * per_value + w.C * 4 + w.H * w.D * w.D * 4
+            + w.P * w.B * w.D * 4)
+
+
+def bench_attend(args, w, device) -> dict:
+    """Time tq_attend (partial and combine kernels) on the workload's shape:
+    scores [P,B,S] and values in the workload's key layout and codebook size."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+
+    bits = w.bits if w.layout == "packed" else 0
+    rng = np.random.default_rng([w.seed, 7])
+    Pi_v = np.stack([synth.haar_rotation(rng, w.D) for _ in range(w.H)])
+    cb = synth.timing_codebook(w.seed, w.C, w.D)
+    idx, norm = synth.timing_value_streams(w.seed, w.P, w.S, w.D, w.C, w.layout, bits)
+    scores = synth.timing_scores(w.seed, w.P, w.B, w.S)
+    shared = {"Pi_v": torch.from_numpy(Pi_v).to(device), "cb": torch.from_numpy(cb).to(device)}
+    base = {"idx": torch.from_numpy(idx).to(device), "norm": torch.from_numpy(norm).to(device),
+            "scores": torch.from_numpy(scores).to(device)}
+    nbytes = attend_bytes(w)
+    nsets = max(2, min(64, math.ceil(RING_BYTES / nbytes)))
+    wsb = tq.tq_attend_workspace_bytes(w.P, w.B, w.S, w.D)
+    ring = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in base.items()}
+        s["values"] = tq.Values(w.layout, s["idx"], s["norm"], bits)
+        s["out"] = torch.empty((w.P, w.B, w.D), dtype=torch.float32, device=device)
+        s["ws"] = torch.empty(wsb, dtype=torch.uint8, device=device)
+        ring.append(s)
+    scale = 1.0 / math.sqrt(w.D)
+
+    def launch(s):
+        tq.tq_attend(s["scores"], s["values"], shared["cb"], shared["Pi_v"], scale, s["out"], s["ws"])
+
+    for i in range(args.warmup):
+        launch(ring[i % nsets])
+    torch.cuda.synchronize()
+    steps = args.steps
+    chunks = [nsets] * (steps // nsets) + ([steps % nsets] if steps % nsets else [])
+    graphs = {}
+    for n in sorted(set(chunks)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                launch(ring[i])
+        graphs[n] = g
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for n in chunks:
+        graphs[n].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    achieved = nbytes / (us * 1e-6) / 1e9
+    log(f"attend: {steps} calls, {us:.2f} us per call, {achieved:.0f} GB/s algorithmic")
+    out = {
+        "metric": "attention outputs/sec (softmax over scores, compressed-value aggregation)",
+        "value": w.P * w.B / (us * 1e-6),
+        "unit": "query outputs/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate",
+        "data": "synthetic: seeded random value codes and norms, N(0, 16) scores, Haar value rotation",
+        "config": {"workload": w.name, "path": "attend", "P": w.P, "H": w.H, "B": w.B, "S": w.S, "D": w.D,
+                   "C": w.C, "layout": w.layout, "bits": w.bits, "scale": scale},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "attend_partial + attend_combine", "bytes_per_launch": nbytes,
+                     "avg_launch_us": us, "workspace_bytes": wsb},
+        "ring_sets": nsets,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import attend as oa
+        from oracle import pack as opk
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        idx0 = idx[0] if w.layout == "unpacked" else opk.unpack_indices(idx[0], w.bits, w.D)
+        n0 = norm[0].astype(np.float64)
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3:
+            t1 = time.perf_counter()
+            oa.attend_rotated(scores[0], idx0, n0, Pi_v[0], cb, scale)
+            times.append(time.perf_counter() - t1)
+        med = sorted(times)[len(times) // 2]
+        out["cpu_baseline"] = {"value": w.B / med, "unit": "query outputs/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"problem 0 (B={w.B}, S={w.S}, D={w.D}) through the float64 oracle, "
+                                         f"median of {len(times)} runs ({sum(times):.1f} s total)"}
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -365,6 +479,9 @@ def main() -> int:
     w = synth.workload(args.workload)
     if args.path == "compress":
         print(json.dumps(bench_compress(args, w, device)), flush=True)
+        return 0
+    if args.path == "attend":
+        print(json.dumps(bench_attend(args, w, device)), flush=True)
         return 0
     kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, args.kernel)
     log(f"workload {w.describe()} kernel {kname}")

@@ -177,7 +177,7 @@ int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat, con
 
 size_t tq_attend_workspace_bytes(int P, int B, int S, int D) {
     if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
-    const int64_t n = (int64_t)P * B * tq::attend_chunks(P, B, S) * (D + 2) * (int64_t)sizeof(float);
+    const int64_t n = (int64_t)P * B * tq::attend_chunks(P, B, S, D) * (D + 2) * (int64_t)sizeof(float);
     return (size_t)n;
 }
 

@@ -5,19 +5,32 @@
 // Pi_v, codebook, one norm per vector), and
 //   o_b = Pi_v^T sum_s p_bs ||v_s|| c[idx_s],   p_b = softmax(scale * scores_b).
 //
-// Split over key ranges (split-KV). attend_partial_kernel: one workgroup per
-// (key chunk, 32-query block, problem); it finds the chunk's maximum of
-// scale*score per query and the chunk's largest norm, then each wavefront owns
-// 32 output coordinates and accumulates, over the chunk's 32-key tiles,
-//   acc[b][d] = sum_s exp(scale*score_bs - m_b) ||v_s|| c[idx_sd]
-// on the matrix cores: v_mfma_f32_32x32x16_f16 with the queries as rows, the
-// wavefront's coordinates as columns and 16 keys per contraction step. Both
-// operands are split into f16 hi/lo parts (three products: P_hi V_hi, P_lo V_hi,
-// P_hi V_lo) after power-of-two scales: the weights are scaled so the chunk's
-// largest possible weight (its largest norm) sits just below 2^14, which keeps
-// every weight that matters out of f16's subnormal range. It writes
-// (m, l, acc) per (chunk, query). attend_combine_kernel merges the chunks of one
-// query and applies Pi_v^T once.
+// Split over key ranges (split-KV). attend_partial_kernel: one workgroup of four
+// wavefronts per (key chunk, group of query tiles, problem). A wavefront owns one
+// query tile and a share of the chunk's keys and runs an online softmax over
+// them: a running reference maximum per query, raised (and the accumulator
+// rescaled) only when a step's maximum exceeds it by more than kTau, so the
+// rescale is rare. The weighted sum
+//   acc[d][b] = sum_s exp(scale*score_bs - m_b) ||v_s|| c[idx_sd]
+// runs on the matrix cores with the value coordinates as rows, the queries as
+// columns and keys as the contraction, so that each lane's accumulators belong
+// to one query:
+//  - wide (B > 8): v_mfma_f32_32x32x16_f16, 32 queries per tile, three products
+//    of f16 hi/lo parts (V_hi W_hi, V_lo W_hi, V_hi W_lo);
+//  - narrow (B <= 8): v_mfma_f32_16x16x32_f16, the weights' hi parts in
+//    columns 0-7 and lo parts in columns 8-15, so two products cover all three
+//    terms.
+// Weights carry the value norms, scaled by a power of two that tracks the
+// largest norm seen, and codebook entries are scaled by a power of two, so
+// every f16 operand stays in the normal range. The wavefronts sharing a query
+// tile merge through LDS and the workgroup writes (m, l, acc) per query and
+// chunk. attend_combine_kernel merges the chunks of one query and applies
+// Pi_v^T once.
+#include <math.h>
+
+#include <algorithm>
+#include <type_traits>
+
 #include "tq_common.hpp"
 
 namespace tq {
@@ -25,42 +38,41 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef _Float16 f16x8u __attribute__((ext_vector_type(8), aligned(2)));
 
-constexpr int kAttendTile = 32;           // keys per contraction tile (two MFMA steps)
+enum AttendMode { kWide = 0, kNarrow = 1 };
+
+// MFMA geometry: ROWS coordinates per tile (lanes n = lane % ROWS), KG lane
+// groups along the contraction (g = lane / ROWS), KSTEP keys per product, Q
+// queries per tile.
+template <int MODE> struct Geo;
+template <> struct Geo<kWide> {
+    static constexpr int ROWS = 32, KG = 2, KSTEP = 16, Q = 32;
+};
+template <> struct Geo<kNarrow> {
+    static constexpr int ROWS = 16, KG = 4, KSTEP = 32, Q = 8;
+};
+
+constexpr int kWaves = 4;          // wavefronts per workgroup
+constexpr float kTau = 5.5f;       // rescale when a step max passes the reference by more (e^5.5 < 2^8)
+constexpr int kNormBits = 4;       // scaled norms stay below 2^(kNormBits + 2) until the next rescale
+constexpr int kTargetBlocks = 512; // workgroups one call aims for (two per compute unit)
+constexpr int kComputeUnits = 256; // MI355X
+constexpr int kPartialShare = 8;   // partial results at most 1/8 of the bytes a chunk reads
 
 union H8 {
     f16x8 h;
     uint32_t u[4];
 };
 
-__device__ __forceinline__ float pow2_below_2e14(float maxabs) {
-    // a power of two bringing maxabs into [2^13, 2^14); 1 if maxabs is 0 or not finite
+__device__ __forceinline__ float pow2_below(float maxabs, int top) {
+    // a power of two bringing maxabs into [2^(top-1), 2^top); 1 if maxabs is 0 or not finite
     if (!(maxabs > 0.f) || !(maxabs < 3.0e38f)) return 1.f;
     int e;
     (void)frexpf(maxabs, &e);
-    return ldexpf(1.f, min(126, max(-126, 14 - e)));
-}
-
-// Index of coordinate d of value s. Unpacked: one byte; packed: BITS bits at
-// bit BITS*d of the value's LSB-first byte string.
-template <int LAYOUT, int BITS, int D>
-__device__ __forceinline__ uint32_t value_index(const uint8_t* __restrict__ idx, int64_t s, int d) {
-    if constexpr (LAYOUT == 0) {
-        return idx[s * D + d];
-    } else {
-        constexpr int ROW = D * BITS / 8;
-        const int bit = BITS * d;
-        // two aligned dwords cover any field (rows are multiples of 4 bytes for D % 32 == 0)
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(idx + s * ROW) + bit / 32;
-        const uint64_t both = (uint64_t)w[0] | ((bit % 32 > 32 - BITS) ? (uint64_t)w[1] << 32 : 0ull);
-        return (uint32_t)(both >> (bit % 32)) & ((1u << BITS) - 1u);
-    }
-}
-
-template <int LAYOUT>
-__device__ __forceinline__ float value_norm(const void* __restrict__ norm, int64_t s) {
-    if constexpr (LAYOUT == 0) return reinterpret_cast<const float*>(norm)[s];
-    else return (float)reinterpret_cast<const _Float16*>(norm)[s];
+    return ldexpf(1.f, min(126, max(-126, top - e)));
 }
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -76,58 +88,65 @@ __device__ __forceinline__ void lut4(uint32_t x, const uint32_t (&tab)[4], uint3
     o1 = perm(hi, lo, 0x07030602u);
 }
 
-template <int LAYOUT, int BITS, int D>
-__global__ __launch_bounds__(D * 2) void attend_partial_kernel(
-    const float* __restrict__ scores, const uint8_t* __restrict__ idx, const void* __restrict__ norm,
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
+
+// Raw loads of one step for one lane: 8 scores of its query, 8 norms (fp32
+// bits, or fp16 pairs), and per key the one or two dwords holding its value
+// bits. Kept as loaded, so that the loads of the next step can be in flight
+// while this one is computed.
+template <int LAYOUT>
+struct Raw {
+    float sc[8];
+    uint32_t nr[8];
+    uint32_t vlo[8], vhi[8];
+};
+
+template <int LAYOUT, int BITS, int D, int MODE, int QTW, int NT>
+__global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
+    const float* __restrict__ scores, const uint8_t* __restrict__ vidx, const void* __restrict__ vnorm,
     const float* __restrict__ codebook, int C, float scale, float* __restrict__ ws,
-    int B, int S, int chunk, int nchunks) {
-    constexpr int NW = D / 32;               // wavefronts: one per 32 output coordinates
-    constexpr int NT = NW * 64;
-    __shared__ float red[NT];
-    __shared__ float rowmax[32];
-    __shared__ float sh_nmax;
+    int B, int S, int chunk, int nch) {
+    using G = Geo<MODE>;
+    constexpr int DB = NT * G::ROWS;               // coordinates per workgroup
+    constexpr int DBLK = D / DB;                   // workgroups along the coordinates
+    constexpr int KW = kWaves / QTW;               // wavefronts sharing one query tile
+    constexpr int DP = DB + 1;                     // LDS row stride (consecutive queries on distinct banks)
+    constexpr int BW = LAYOUT == 0 ? 8 : BITS;     // bits per coordinate
+    constexpr int W = NT * BW;                     // value bits per lane per key
+    constexpr int ROWB = D * BW / 8;               // bytes per value row
+    static_assert(DBLK * DB == D && W <= 64 && ROWB % 4 == 0, "tiling");
+    __shared__ float red_acc[kWaves][G::Q][DP];
+    __shared__ float red_m[kWaves][G::Q];
+    __shared__ float red_l[kWaves][G::Q];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = blockIdx.x;
-    const int b0 = blockIdx.y * 32;
+    const int qtw = wave % QTW;
+    const int kw = wave / QTW;
     const int p = blockIdx.z;
-    const int rows = min(32, B - b0);
+    const int c = blockIdx.x;
+    const int tg = blockIdx.y / DBLK;                  // group of query tiles
+    const int db = blockIdx.y % DBLK;                  // coordinate block
+    const int q0 = (tg * QTW + qtw) * G::Q;            // first query of this wavefront's tile
+    const int n = lane % G::ROWS;
+    const int g = lane / G::ROWS;
+    const int ql = MODE == kWide ? n : (n & 7);        // query of this lane's weight column
+    const int part = MODE == kWide ? 0 : (n >> 3);     // narrow: 0 = hi column, 1 = lo column
+    const bool qvalid = q0 + ql < B;
+    const float* srow = scores + ((int64_t)p * B + min(q0 + ql, B - 1)) * S;
     const int s_begin = c * chunk;
     const int s_end = min(S, s_begin + chunk);
     const int64_t key0 = (int64_t)p * S;
-    const float* sc_p = scores + ((int64_t)p * B + b0) * S;
+    // value bits of coordinates db*DB + NT*n .. + NT-1: dword k0 of the row, and
+    // the next one when the field runs into it
+    const int vbit = BW * (db * DB + NT * n);
+    const int k0 = vbit >> 5;
+    const int vsh = vbit & 31;
+    const bool two = vsh + W > 32;
+    const uint8_t* vbase = vidx + key0 * ROWB + 4 * k0;
 
-    // ---- chunk maxima: m_b = max scale*score (rows past B read row rows-1) and
-    //      the largest norm
-    {
-        const int b = tid % 32, part = tid / 32;
-        const float* row = sc_p + (int64_t)min(b, rows - 1) * S;
-        float m = -INFINITY;
-        for (int s = s_begin + part; s < s_end; s += NT / 32) m = fmaxf(m, scale * row[s]);
-        red[tid] = m;
-        float n = 0.f;
-        for (int s = s_begin + tid; s < s_end; s += NT) n = fmaxf(n, fabsf(value_norm<LAYOUT>(norm, key0 + s)));
-        __syncthreads();
-        if (tid < 32) {
-            float mm = red[tid];
-            for (int k = 1; k < NT / 32; ++k) mm = fmaxf(mm, red[tid + 32 * k]);
-            rowmax[tid] = mm;
-        }
-        __syncthreads();
-        red[tid] = n;
-        __syncthreads();
-        if (tid == 0) {
-            float nn = 0.f;
-            for (int k = 0; k < NT; ++k) nn = fmaxf(nn, red[k]);
-            sh_nmax = nn;
-        }
-        __syncthreads();
-    }
-    const float wscale = pow2_below_2e14(sh_nmax);    // weights p' * wscale stay below 2^14
-
-    // codebook scale and byte tables (hi and lo f16 parts)
+    // codebook tables (hi and lo f16 parts of the entries times a power of two)
     float cbv[8];
     float mc = 0.f;
 #pragma unroll
@@ -135,7 +154,7 @@ __global__ __launch_bounds__(D * 2) void attend_partial_kernel(
         cbv[k] = k < C ? codebook[k] : 0.f;
         mc = fmaxf(mc, fabsf(cbv[k]));
     }
-    const float cscale = pow2_below_2e14(mc);
+    const float cscale = pow2_below(mc, 14);
     uint32_t tab_hi[4] = {0u, 0u, 0u, 0u}, tab_lo[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -150,104 +169,379 @@ __global__ __launch_bounds__(D * 2) void attend_partial_kernel(
         tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
     }
 
-    // ---- accumulate: lane (query r = lane % 32, key group g = lane / 32) for the
-    //      A operand; lane (coordinate d = 32 wave + lane % 32, key group g) for B
-    const int r = lane & 31;
-    const int g = lane >> 5;
-    const int d = 32 * wave + r;
-    const float mr = rowmax[r];
-    const float* srow = sc_p + (int64_t)min(r, rows - 1) * S;
-    f32x16 acc;
+    using Acc = typename std::conditional<MODE == kWide, f32x16, f32x4>::type;
+    constexpr int NV = MODE == kWide ? 16 : 4;
+    Acc acc[NT];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    float lsum = 0.f;                          // sum of exp over this lane's keys (query r)
-    for (int t0 = s_begin; t0 < s_end; t0 += kAttendTile) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int sb = t0 + 16 * ks + 8 * g;   // this lane's 8 keys of the step
-            H8 phi, plo, vhi, vlo;
+        for (int v = 0; v < NV; ++v) acc[t][v] = 0.f;
+    float M = -INFINITY;      // reference maximum of scale*score for query ql
+    float lsum = 0.f;         // sum of exp(scale*score - M) over this lane's keys
+    float nexp = -1000.f;     // norms are scaled by 2^-nexp ...
+    float nlim = 0.f;         // ... and must stay below nlim = 2^(nexp + kNormBits + 2)
+
+    // this wavefront's steps: keys s_begin + (kw + KW*i)*KSTEP + [0, KSTEP)
+    const int span = s_end - s_begin - kw * G::KSTEP;
+    const int ntot = span > 0 ? (span + KW * G::KSTEP - 1) / (KW * G::KSTEP) : 0;
+    const int nfull = span >= G::KSTEP ? (span - G::KSTEP) / (KW * G::KSTEP) + 1 : 0;
+    auto first_key = [&](int i) { return s_begin + (kw + KW * i) * G::KSTEP + 8 * g; };
+
+    auto load_full = [&](Raw<LAYOUT>& r, int sk) {
+        const f32x4u a = *reinterpret_cast<const f32x4u*>(srow + sk);
+        const f32x4u b = *reinterpret_cast<const f32x4u*>(srow + sk + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r.sc[e] = a[e];
+            r.sc[4 + e] = b[e];
+        }
+        if constexpr (LAYOUT == 0) {
+            const uint32_t* np = reinterpret_cast<const uint32_t*>(vnorm) + key0 + sk;
+            typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(4)));
+            const u32x4u x = *reinterpret_cast<const u32x4u*>(np);
+            const u32x4u y = *reinterpret_cast<const u32x4u*>(np + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r.nr[e] = x[e];
+                r.nr[4 + e] = y[e];
+            }
+        } else {
+            typedef uint32_t u32x4h __attribute__((ext_vector_type(4), aligned(2)));
+            const u32x4h x = *reinterpret_cast<const u32x4h*>(reinterpret_cast<const uint16_t*>(vnorm) + key0 + sk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r.nr[e] = x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(vbase + (int64_t)(sk + e) * ROWB);
+            r.vlo[e] = w[0];
+            r.vhi[e] = w[two ? 1 : 0];     // in-row either way
+        }
+    };
+    auto load_tail = [&](Raw<LAYOUT>& r, int sk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s = min(sk + e, s_end - 1);
+            r.sc[e] = srow[s];
+            if constexpr (LAYOUT == 0) {
+                r.nr[e] = reinterpret_cast<const uint32_t*>(vnorm)[key0 + s];
+            } else {
+                const uint32_t h = reinterpret_cast<const uint16_t*>(vnorm)[key0 + s];
+                if (e % 2 == 0) r.nr[e / 2] = h;
+                else r.nr[e / 2] |= h << 16;
+            }
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(vbase + (int64_t)s * ROWB);
+            r.vlo[e] = w[0];
+            r.vhi[e] = w[two ? 1 : 0];
+        }
+    };
+    auto compute = [&](const Raw<LAYOUT>& r, int sk, int lim) {
+        // step maximum of the lane's query over the step's keys
+        float z[8], nv[8];
+        float ms = -INFINITY, nm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            z[e] = (qvalid && sk + e < lim) ? scale * r.sc[e] : -INFINITY;
+            if constexpr (LAYOUT == 0) nv[e] = __builtin_bit_cast(float, r.nr[e]);
+            else nv[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.nr[e / 2] >> (16 * (e % 2))));
+            ms = fmaxf(ms, z[e]);
+            nm = fmaxf(nm, fabsf(nv[e]));
+        }
+        ms = xor_max(ms, 32);
+        if constexpr (MODE == kNarrow) ms = xor_max(ms, 16);
+        const bool need_m = ms > M + kTau;
+        if (__any(need_m || nm >= nlim)) {
+            // rescale: new reference maximum for the lanes that need it, and a new
+            // norm scale for the whole wavefront if a norm outgrew the current one
+            float nw = nm;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) nw = xor_max(nw, m);
+            float fac = 1.f;
+            if (nw >= nlim) {
+                int e2;
+                (void)frexpf(nw, &e2);
+                const float ne = nw > 0.f ? (float)(e2 - kNormBits) : 0.f;
+                fac = exp2f(nexp - ne);
+                nexp = ne;
+                nlim = exp2f(ne + kNormBits + 2);
+            }
+            const float Mn = need_m ? ms : M;
+            const float fm = need_m ? __expf(M - Mn) : 1.f;
+            M = Mn;
+            lsum *= fm;
+            fac *= fm;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[t][v] *= fac;
+        }
+        const float nscale = exp2f(-nexp);
+        H8 whi, wlo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float w = z[e] == -INFINITY ? 0.f : __expf(z[e] - M);
+            lsum += w;
+            const float x = w * nv[e] * nscale;
+            const _Float16 h = (_Float16)x;
+            whi.h[e] = h;
+            wlo.h[e] = (_Float16)(x - (float)h);
+        }
+        uint64_t vb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vb[e] = ((two ? (uint64_t)r.vhi[e] << 32 : 0ull) | r.vlo[e]) >> vsh;
+        // value operands per tile and the products
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
             uint32_t sel0 = 0, sel1 = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = sb + e;
-                const bool in = s < s_end;
-                const int sc_ = in ? s : s_end - 1;
-                const float w = in ? __expf(scale * srow[sc_] - mr) : 0.f;
-                lsum += w;
-                const float x = w * value_norm<LAYOUT>(norm, key0 + sc_) * wscale;
-                const _Float16 h = (_Float16)x;
-                phi.h[e] = h;
-                plo.h[e] = (_Float16)(x - (float)h);
-                const uint32_t iv = value_index<LAYOUT, BITS, D>(idx, key0 + sc_, d);
-                if (e < 4) sel0 |= iv << (8 * e);
-                else sel1 |= iv << (8 * (e - 4));
+            for (int e = 0; e < 4; ++e) {
+                sel0 |= ((uint32_t)(vb[e] >> (BW * t)) & ((1u << BW) - 1u)) << (8 * e);
+                sel1 |= ((uint32_t)(vb[4 + e] >> (BW * t)) & ((1u << BW) - 1u)) << (8 * e);
             }
+            H8 vhi, vlo;
             lut4(sel0, tab_hi, vhi.u[0], vhi.u[1]);
             lut4(sel1, tab_hi, vhi.u[2], vhi.u[3]);
             lut4(sel0, tab_lo, vlo.u[0], vlo.u[1]);
             lut4(sel1, tab_lo, vlo.u[2], vlo.u[3]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(phi.h, vhi.h, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(plo.h, vhi.h, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(phi.h, vlo.h, acc, 0, 0, 0);
-        }
-    }
-    // l_b: the two key groups of query r sit in lanes r and r + 32
-    lsum += __shfl_xor(lsum, 32);
-
-    // ---- write (m, l, acc) of this chunk: ws layout [P][B][nchunks][D + 2]
-    const float unscale = 1.f / (wscale * cscale);   // powers of two: exact
+            if constexpr (MODE == kWide) {
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vhi.h, whi.h, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vlo.h, whi.h, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vhi.h, wlo.h, acc[t], 0, 0, 0);
+            } else {
+                H8 wb, wh;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int row = 8 * (v >> 2) + 4 * g + (v & 3);   // output element v: query row, coordinate d
-        if (row < rows) {
-            float* rec = ws + (((int64_t)p * B + b0 + row) * nchunks + c) * (D + 2);
-            rec[2 + 32 * wave + r] = acc[v] * unscale;
+                for (int k = 0; k < 4; ++k) {
+                    wb.u[k] = part ? wlo.u[k] : whi.u[k];
+                    wh.u[k] = part ? 0u : whi.u[k];
+                }
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi.h, wb.h, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo.h, wh.h, acc[t], 0, 0, 0);
+            }
+        }
+    };
+
+    if (q0 < B) {
+        // full steps, two buffers: the next step's loads are in flight while a step
+        // is computed (a prefetch past the last full step re-reads that step)
+        if (nfull > 0) {
+            Raw<LAYOUT> ra, rb;
+            load_full(ra, first_key(0));
+            int i = 0;
+            for (; i + 1 < nfull; i += 2) {
+                load_full(rb, first_key(i + 1));
+                compute(ra, first_key(i), INT32_MAX);
+                load_full(ra, first_key(min(i + 2, nfull - 1)));
+                compute(rb, first_key(i + 1), INT32_MAX);
+            }
+            if (i < nfull) compute(ra, first_key(i), INT32_MAX);
+        }
+        if (ntot > nfull) {
+            Raw<LAYOUT> rt;
+            load_tail(rt, first_key(nfull));
+            compute(rt, first_key(nfull), s_end);
         }
     }
-    if (wave == 0 && g == 0 && r < rows) {
-        float* rec = ws + (((int64_t)p * B + b0 + r) * nchunks + c) * (D + 2);
-        rec[0] = mr;
-        rec[1] = lsum;
+
+    // ---- per-wavefront results to LDS: query ql's m, l and acc (true scale)
+    lsum += __shfl_xor(lsum, 32);
+    if constexpr (MODE == kNarrow) {
+        lsum += __shfl_xor(lsum, 16);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[t][v] += __shfl_xor(acc[t][v], 8);   // hi + lo columns
+    }
+    const float unscale = exp2f(nexp) / cscale;
+    if (g == 0 && part == 0) {
+        red_m[wave][ql] = M;
+        red_l[wave][ql] = lsum;
+    }
+    if (part == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int row = MODE == kWide ? 8 * (v >> 2) + 4 * g + (v & 3) : 4 * g + v;
+                red_acc[wave][ql][NT * row + t] = acc[t][v] * unscale;
+            }
+    }
+    __syncthreads();
+
+    // ---- merge the KW wavefronts of each query tile and write the records
+    for (int i = tid; i < QTW * G::Q * DB; i += kWaves * 64) {
+        const int d = i % DB;
+        const int qi = (i / DB) % G::Q;
+        const int tq = i / (DB * G::Q);
+        const int q = (tg * QTW + tq) * G::Q + qi;
+        if (q >= B) continue;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) Mx = fmaxf(Mx, red_m[k * QTW + tq][qi]);
+        float a = 0.f, l = 0.f;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            const int w = k * QTW + tq;
+            const float f = red_m[w][qi] == -INFINITY ? 0.f : __expf(red_m[w][qi] - Mx);
+            a = fmaf(red_acc[w][qi][d], f, a);
+            l = fmaf(red_l[w][qi], f, l);
+        }
+        float* rec = ws + (((int64_t)p * B + q) * nch + c) * (D + 2);
+        rec[2 + db * DB + d] = a;
+        if (db == 0 && d == 0) {
+            rec[0] = Mx;
+            rec[1] = l;
+        }
     }
 }
 
+// One workgroup per (query, problem): merge the chunks' (m, l, acc) and apply
+// Pi_v^T: out_j = sum_d Pi_v[d][j] a_d with a = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M).
 template <int D>
-__global__ __launch_bounds__(D) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
-                                                           float* __restrict__ out, int H, int B, int nchunks) {
+__global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
+                                                             float* __restrict__ out, int H, int B, int nch) {
+    constexpr int DL = (D + 63) / 64;      // coordinates per lane
+    constexpr int NB = 4;                  // chunks per wavefront per batch of loads
+    __shared__ float part_a[4][D];
+    __shared__ float part_l[4];
+    __shared__ float wmax[4];
     __shared__ float a[D];
-    const int j = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
     const int p = blockIdx.y;
-    const float* rec = ws + ((int64_t)p * B + b) * nchunks * (D + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, rec[c * (D + 2)]);
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-        const float f = __expf(rec[c * (D + 2)] - M);
-        den = fmaf(rec[c * (D + 2) + 1], f, den);
-        num = fmaf(rec[c * (D + 2) + 2 + j], f, num);
-    }
-    a[j] = num / den;
+    const float* rec = ws + ((int64_t)p * B + b) * nch * (D + 2);
+
+    float m = -INFINITY;
+    for (int c = tid; c < nch; c += 256) m = fmaxf(m, rec[(int64_t)c * (D + 2)]);
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) m = xor_max(m, s);
+    if (lane == 0) wmax[wave] = m;
     __syncthreads();
-    // o_j = sum_d Pi_v[d][j] a_d
-    const float* P = Pi_v + (int64_t)(p % H) * D * D;
-    float o = 0.f;
-    for (int dd = 0; dd < D; ++dd) o = fmaf(P[(int64_t)dd * D + j], a[dd], o);
-    out[((int64_t)p * B + b) * D + j] = o;
+    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+    float acc[DL];
+#pragma unroll
+    for (int k = 0; k < DL; ++k) acc[k] = 0.f;
+    float den = 0.f;
+    for (int c0 = wave; c0 < nch; c0 += 4 * NB) {
+        float mv[NB], lv[NB], av[NB][DL];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int c = min(c0 + 4 * j, nch - 1);
+            const float* r = rec + (int64_t)c * (D + 2);
+            mv[j] = r[0];
+            lv[j] = r[1];
+#pragma unroll
+            for (int k = 0; k < DL; ++k) av[j][k] = r[2 + min(lane + 64 * k, D - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const float f = c0 + 4 * j < nch ? __expf(mv[j] - M) : 0.f;
+            den = fmaf(lv[j], f, den);
+#pragma unroll
+            for (int k = 0; k < DL; ++k) acc[k] = fmaf(av[j][k], f, acc[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < DL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) part_a[wave][d] = acc[k];
+    }
+    if (lane == 0) part_l[wave] = den;
+    __syncthreads();
+    if (tid < D) {
+        const float l = part_l[0] + part_l[1] + part_l[2] + part_l[3];
+        a[tid] = (part_a[0][tid] + part_a[1][tid] + part_a[2][tid] + part_a[3][tid]) / l;
+    }
+    __syncthreads();
+    if (tid < D) {
+        const float* P = Pi_v + (int64_t)(p % H) * D * D;
+        float o = 0.f;
+#pragma unroll 16
+        for (int d = 0; d < D; ++d) o = fmaf(P[(int64_t)d * D + tid], a[d], o);
+        out[((int64_t)p * B + b) * D + tid] = o;
+    }
+}
+
+struct Plan {
+    int mode;    // kWide or kNarrow
+    int qtw;     // query tiles per workgroup (1, 2 or 4)
+    int gy;      // groups of query tiles
+    int nt;      // tiles (coordinates per lane) per wavefront
+    int dblk;    // workgroups along the coordinates
+    int nch;     // key chunks
+    int chunk;   // keys per chunk
+};
+
+Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
+    Plan pl;
+    pl.mode = B <= 8 ? kNarrow : kWide;
+    const int Q = pl.mode == kWide ? Geo<kWide>::Q : Geo<kNarrow>::Q;
+    const int rows = pl.mode == kWide ? Geo<kWide>::ROWS : Geo<kNarrow>::ROWS;
+    const int kstep = pl.mode == kWide ? Geo<kWide>::KSTEP : Geo<kNarrow>::KSTEP;
+    const int ntiles = (B + Q - 1) / Q;
+    pl.qtw = ntiles >= 4 ? 4 : ntiles >= 2 ? 2 : 1;
+    pl.gy = (ntiles + pl.qtw - 1) / pl.qtw;
+    const int unit = kstep * (kWaves / pl.qtw);      // keys of one step of every wavefront sharing a tile
+    // keys per chunk at least: the partial results stay under 1/kPartialShare of
+    // the bytes the chunk reads (its scores and values)
+    const int64_t bq = std::min<int64_t>(B, (int64_t)Q * pl.qtw);
+    const int64_t vbytes = (layout == 0 ? D + 4 : (int64_t)D * bits / 8 + 2);
+    int64_t cmin = (kPartialShare * bq * (D + 2) * 4 + bq * 4 + vbytes - 1) / (bq * 4 + vbytes);
+    cmin = (cmin + unit - 1) / unit * unit;
+    const int64_t blocks = (int64_t)P * pl.gy;
+    int64_t n = (kTargetBlocks + blocks - 1) / blocks;
+    const int64_t most = (S + cmin - 1) / cmin;
+    if (n > most) n = most;
+    if (n < 1) n = 1;
+    const int64_t per = (S + n - 1) / n;
+    pl.chunk = (int)((per + unit - 1) / unit * unit);
+    pl.nch = (S + pl.chunk - 1) / pl.chunk;
+    // split the coordinates until there is about one workgroup per compute unit
+    const int ntfull = D / rows;
+    pl.dblk = 1;
+    while (pl.dblk < 4 && ntfull / (2 * pl.dblk) >= 1 && blocks * pl.nch * pl.dblk < kComputeUnits) pl.dblk *= 2;
+    pl.nt = ntfull / pl.dblk;
+    return pl;
+}
+
+template <int LAYOUT, int BITS, int D, int MODE, int QTW>
+hipError_t launch_partial_q(const Plan& pl, const float* scores, ValueStreams v, const float* codebook, int C,
+                            float scale, float* ws, int P, int B, int S, hipStream_t stream) {
+    constexpr int NTF = D / Geo<MODE>::ROWS;
+    const dim3 grid((unsigned)pl.nch, (unsigned)(pl.gy * pl.dblk), (unsigned)P);
+    const dim3 block(kWaves * 64);
+#define TQ_PARTIAL(NTV)                                                                                        \
+    hipLaunchKernelGGL((attend_partial_kernel<LAYOUT, BITS, D, MODE, QTW, NTV>), grid, block, 0, stream, scores, \
+                       v.idx, v.norm, codebook, C, scale, ws, B, S, pl.chunk, pl.nch)
+    constexpr int NT2 = NTF / 2 > 0 ? NTF / 2 : 1;
+    constexpr int NT4 = NTF / 4 > 0 ? NTF / 4 : 1;
+    if (pl.nt == NTF) TQ_PARTIAL(NTF);
+    else if (pl.nt == NT2) TQ_PARTIAL(NT2);
+    else TQ_PARTIAL(NT4);
+#undef TQ_PARTIAL
+    return hipGetLastError();
+}
+
+template <int LAYOUT, int BITS, int D, int MODE>
+hipError_t launch_partial(const Plan& pl, const float* scores, ValueStreams v, const float* codebook, int C,
+                          float scale, float* ws, int P, int B, int S, hipStream_t stream) {
+    if (pl.qtw == 4) return launch_partial_q<LAYOUT, BITS, D, MODE, 4>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream);
+    if (pl.qtw == 2) return launch_partial_q<LAYOUT, BITS, D, MODE, 2>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream);
+    return launch_partial_q<LAYOUT, BITS, D, MODE, 1>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream);
 }
 
 template <int LAYOUT, int BITS, int D>
 hipError_t launch_attend_d(const float* scores, ValueStreams v, const float* codebook, int C, const float* Pi_v,
                            float scale, float* out, float* ws, int P, int H, int B, int S, hipStream_t stream) {
-    const int nch = attend_chunks(P, B, S);
-    const int chunk = ((S + nch - 1) / nch + kAttendTile - 1) / kAttendTile * kAttendTile;
-    const int used = (S + chunk - 1) / chunk;
-    hipLaunchKernelGGL((attend_partial_kernel<LAYOUT, BITS, D>), dim3((unsigned)used, (B + 31) / 32, P), dim3(D * 2),
-                       0, stream, scores, v.idx, v.norm, codebook, C, scale, ws, B, S, chunk, used);
-    hipError_t e = hipGetLastError();
+    const Plan pl = make_plan(P, B, S, D, LAYOUT, BITS);
+    const hipError_t e = pl.mode == kWide
+                             ? launch_partial<LAYOUT, BITS, D, kWide>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream)
+                             : launch_partial<LAYOUT, BITS, D, kNarrow>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)B, P), dim3(D), 0, stream, ws, Pi_v, out, H, B,
-                       used);
+    hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)B, P), dim3(256), 0, stream, ws, Pi_v, out, H, B,
+                       pl.nch);
     return hipGetLastError();
 }
 
@@ -261,16 +555,9 @@ hipError_t launch_attend_layout(const float* scores, ValueStreams v, const float
 
 }  // namespace
 
-// Key chunks per (problem, 32-query block): enough workgroups to fill the chip
-// (about 512), each chunk at least one 32-key tile.
-int attend_chunks(int P, int B, int S) {
-    const int64_t blocks = (int64_t)P * ((B + 31) / 32);
-    int64_t n = (512 + blocks - 1) / blocks;
-    const int64_t tiles = (S + kAttendTile - 1) / kAttendTile;
-    if (n > tiles) n = tiles;
-    if (n < 1) n = 1;
-    return (int)n;
-}
+// The unpacked layout reads the most bytes per key, so it has the shortest
+// chunks and the most of them: its count bounds every layout's.
+int attend_chunks(int P, int B, int S, int D) { return make_plan(P, B, S, D, 0, 0).nch; }
 
 bool attend_supported(int layout, int bits, int C, int D) {
     if (C < 1 || C > 8) return false;

@@ -66,9 +66,9 @@ struct ValueStreams {
     const uint8_t* idx;
     const void* norm;
 };
-// Key chunks the attention step splits each (problem, 32-query block) into;
-// the workspace holds P * B * chunks * (D + 2) floats.
-int attend_chunks(int P, int B, int S);
+// Upper bound on the key chunks the attention step splits each problem into
+// (for any value layout); the workspace holds P * B * chunks * (D + 2) floats.
+int attend_chunks(int P, int B, int S, int D);
 bool attend_supported(int layout, int bits, int C, int D);
 hipError_t launch_attend(const float* scores, ValueStreams v, int layout, int bits, const float* codebook, int C,
                          const float* Pi_v, float scale, float* out, float* ws, int P, int H, int B, int S, int D,

@@ -233,8 +233,8 @@ typedef struct tq_values {
 
 /*
  * tq_attend_workspace_bytes: bytes of the workspace tq_attend needs for this
- * shape (0 for an empty shape or invalid sizes). Host-only. The size depends
- * only on (P, B, S, D).
+ * shape with either value layout (0 for an empty shape or invalid sizes).
+ * Host-only. The size depends only on (P, B, S, D).
  */
 size_t tq_attend_workspace_bytes(int P, int B, int S, int D);
 

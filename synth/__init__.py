@@ -12,7 +12,8 @@ with a list, so a problem's data can be drawn without drawing the others):
   ``default_rng([seed, 0, h])`` draws the rotation first, then the projection;
 * keys of problem ``p``: ``default_rng([seed, 1, p])``;
 * queries of all problems: ``default_rng([seed, 2])``;
-* random code streams used only for timing: ``default_rng([seed, 3, p])``.
+* random code streams used only for timing: ``default_rng([seed, 3, p])``;
+* random value streams and scores used only for timing: ``default_rng([seed, 5, p])``.
 
 The rotation is a Haar-random orthogonal matrix (QR of a Gaussian matrix with
 the signs of R's diagonal folded into Q), the QJL projection has iid N(0, 1)
@@ -139,3 +140,35 @@ def timing_code_streams(seed: int, P: int, S: int, D: int, C: int,
             sign[p] = rng.integers(0, 256, size=sign.shape[1:], dtype=np.uint8)
         gamma[p] = rng.uniform(0.2, 0.5, size=S)
     return idx, sign, gamma
+
+
+def timing_value_streams(seed: int, P: int, S: int, D: int, C: int, layout: str, bits: int):
+    """Random but valid compressed-value streams for timing.
+
+    unpacked: idx uint8 [P, S, D] uniform in [0, C), norm float32 [P, S];
+    packed: idx bytes [P, S, D*bits/8] uniform, norm float16 [P, S].
+    Norms are uniform in [0.5, 2] * sqrt(D), the length of a Gaussian vector.
+    """
+    if layout == "unpacked":
+        idx = np.empty((P, S, D), np.uint8)
+        norm = np.empty((P, S), np.float32)
+    elif layout == "packed":
+        idx = np.empty((P, S, D * bits // 8), np.uint8)
+        norm = np.empty((P, S), np.float16)
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    for p in range(P):
+        rng = np.random.default_rng([seed, 5, p])
+        if layout == "unpacked":
+            idx[p] = rng.integers(0, C, size=(S, D), dtype=np.uint8)
+        else:
+            idx[p] = rng.integers(0, 256, size=idx.shape[1:], dtype=np.uint8)
+        norm[p] = rng.uniform(0.5, 2.0, size=S) * np.sqrt(D)
+    return idx, norm
+
+
+def timing_scores(seed: int, P: int, B: int, S: int) -> np.ndarray:
+    """Scores [P, B, S] float32, N(0, 4^2): the spread of raw query-key scores
+    of N(0, 1) queries against keys a few times the unit length."""
+    rng = np.random.default_rng([seed, 6])
+    return (rng.standard_normal((P, B, S), dtype=np.float32) * 4.0).astype(np.float32)

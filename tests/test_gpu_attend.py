@@ -78,6 +78,10 @@ CASES = [
     ("packed", 3, 8, 128, 4, 2, 70, 1500),
     ("packed", 3, 8, 64, 1, 1, 1, 100),
     ("packed", 3, 8, 128, 2, 1, 96, 40000),
+    ("unpacked", 0, 4, 128, 1, 1, 8, 3000),
+    ("packed", 3, 8, 128, 1, 1, 9, 700),
+    ("packed", 2, 4, 64, 1, 1, 161, 2500),
+    ("unpacked", 0, 8, 128, 2, 2, 128, 5000),
 ]
 
 
@@ -172,4 +176,22 @@ def test_score_then_attend():
     ref_scores = np.stack([osc.scores_by_reconstruction(q[p], idx_k[p], sign_k[p], gamma[p].astype(np.float64),
                                                         Pi[p % H], S_mat[p % H], cb) for p in range(P)])
     ref = oracle_out(ref_scores, idx_v, norm, Pi_v, cbv, 1.0 / np.sqrt(D), H)
+    assert rel_err(got, ref) <= SCORE_TOL
+
+
+@pytest.mark.parametrize("B", [3, 40])
+def test_attend_rescales(B):
+    """Scores rising along the keys (the running maximum moves many times), norms
+    growing over six decades with zero norms between (the norm scale moves)."""
+    say(f"attend rescales B={B}")
+    P, H, S, D, C = 1, 1, 4000, 128, 8
+    vals, idx, _, Pi_v, cb = value_case(12, P, H, S, D, C, "unpacked", 0)
+    norm = np.geomspace(1e-3, 1e3, S).astype(np.float32)[None, :]
+    norm[0, ::7] = 0.0
+    vals = tq.Values("unpacked", vals.idx, t(norm))
+    rng = np.random.default_rng(13)
+    ramp = np.linspace(-50.0, 50.0, S)[None, None, :]
+    scores = (ramp + rng.standard_normal((P, B, S)) * 2.0).astype(np.float32)
+    got = tq.tq_attend(t(scores), vals, t(cb), t(Pi_v), 0.3).cpu().numpy()
+    ref = oracle_out(scores, idx, norm.astype(np.float64), Pi_v, cb, 0.3, H)
     assert rel_err(got, ref) <= SCORE_TOL
