@@ -357,6 +357,25 @@ def attend_bytes(w) -> int:
             + w.P * w.B * w.D * 4)
 
 
+def attend_traffic(w):
+    """HBM bytes per tq_attend call (both kernels) from the committed counter
+    record of this workload, if taken with attend.hip as it is now; else None."""
+    import hashlib
+
+    try:
+        with open(os.path.join(ROOT, "profiles", f"tq_attend_{w.name}_counters.json")) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for p in rec["source_files"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes_per_call"]
+
+
 def bench_attend(args, w, device) -> dict:
     """Time tq_attend (partial and combine kernels) on the workload's shape:
     scores [P,B,S] and values in the workload's key layout and codebook size."""
@@ -432,7 +451,7 @@ def bench_attend(args, w, device) -> dict:
         "config": {"workload": w.name, "path": "attend", "P": w.P, "H": w.H, "B": w.B, "S": w.S, "D": w.D,
                    "C": w.C, "layout": w.layout, "bits": w.bits, "scale": scale},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": attend_traffic(w),
                      "kernel": "attend_partial + attend_combine", "bytes_per_launch": nbytes,
                      "avg_launch_us": us, "workspace_bytes": wsb},
         "ring_sets": nsets,

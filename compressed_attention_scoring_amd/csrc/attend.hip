@@ -6,8 +6,8 @@
 //   o_b = Pi_v^T sum_s p_bs ||v_s|| c[idx_s],   p_b = softmax(scale * scores_b).
 //
 // Split over key ranges (split-KV). attend_partial_kernel: one workgroup of four
-// wavefronts per (key chunk, group of query tiles, problem). A wavefront owns one
-// query tile and a share of the chunk's keys and runs an online softmax over
+// wavefronts per (key chunk, group of query tiles, block of coordinates,
+// problem). A wavefront owns one query tile and a share of the chunk's keys and runs an online softmax over
 // them: a running reference maximum per query, raised (and the accumulator
 // rescaled) only when a step's maximum exceeds it by more than kTau, so the
 // rescale is rare. The weighted sum
@@ -60,7 +60,7 @@ constexpr float kTau = 5.5f;       // rescale when a step max passes the referen
 constexpr int kNormBits = 4;       // scaled norms stay below 2^(kNormBits + 2) until the next rescale
 constexpr int kTargetBlocks = 512; // workgroups one call aims for (two per compute unit)
 constexpr int kComputeUnits = 256; // MI355X
-constexpr int kPartialShare = 8;   // partial results at most 1/8 of the bytes a chunk reads
+constexpr int kPartialShare = 4;   // partial results at most 1/4 of the bytes a chunk reads
 
 union H8 {
     f16x8 h;
@@ -109,15 +109,18 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
     using G = Geo<MODE>;
     constexpr int DB = NT * G::ROWS;               // coordinates per workgroup
     constexpr int DBLK = D / DB;                   // workgroups along the coordinates
-    constexpr int KW = kWaves / QTW;               // wavefronts sharing one query tile
+    constexpr int NW = kWaves;
+    constexpr int KW = NW / QTW;                   // wavefronts sharing one query tile
     constexpr int DP = DB + 1;                     // LDS row stride (consecutive queries on distinct banks)
     constexpr int BW = LAYOUT == 0 ? 8 : BITS;     // bits per coordinate
     constexpr int W = NT * BW;                     // value bits per lane per key
     constexpr int ROWB = D * BW / 8;               // bytes per value row
+    // 0: a lane's field never leaves its dword; 2: it always spans two; 1: it depends on the lane
+    constexpr int CROSS = W > 32 ? 2 : (32 % W == 0 ? 0 : 1);
     static_assert(DBLK * DB == D && W <= 64 && ROWB % 4 == 0, "tiling");
-    __shared__ float red_acc[kWaves][G::Q][DP];
-    __shared__ float red_m[kWaves][G::Q];
-    __shared__ float red_l[kWaves][G::Q];
+    __shared__ float red_acc[NW][G::Q][DP];
+    __shared__ float red_m[NW][G::Q];
+    __shared__ float red_l[NW][G::Q];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
     const int vbit = BW * (db * DB + NT * n);
     const int k0 = vbit >> 5;
     const int vsh = vbit & 31;
-    const bool two = vsh + W > 32;
+    const bool two = CROSS == 2 || (CROSS == 1 && vsh + W > 32);
     const uint8_t* vbase = vidx + key0 * ROWB + 4 * k0;
 
     // codebook tables (hi and lo f16 parts of the entries times a power of two)
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
     __syncthreads();
 
     // ---- merge the KW wavefronts of each query tile and write the records
-    for (int i = tid; i < QTW * G::Q * DB; i += kWaves * 64) {
+    for (int i = tid; i < QTW * G::Q * DB; i += NW * 64) {
         const int d = i % DB;
         const int qi = (i / DB) % G::Q;
         const int tq = i / (DB * G::Q);
@@ -396,15 +399,20 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
 
 // One workgroup per (query, problem): merge the chunks' (m, l, acc) and apply
 // Pi_v^T: out_j = sum_d Pi_v[d][j] a_d with a = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M).
+// Loads are issued in batches (NB chunk records per wavefront, all of a
+// thread's share of Pi_v) so each phase costs about one memory round trip.
 template <int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
                                                              float* __restrict__ out, int H, int B, int nch) {
     constexpr int DL = (D + 63) / 64;      // coordinates per lane
-    constexpr int NB = 4;                  // chunks per wavefront per batch of loads
+    constexpr int NB = 8;                  // chunk records per wavefront per batch of loads
+    constexpr int JP = 256 / D;            // threads per output coordinate in the product with Pi_v
+    constexpr int DJ = D / JP;             // coordinates each of them sums
     __shared__ float part_a[4][D];
     __shared__ float part_l[4];
     __shared__ float wmax[4];
     __shared__ float a[D];
+    __shared__ float po[JP][D];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -455,12 +463,22 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
         a[tid] = (part_a[0][tid] + part_a[1][tid] + part_a[2][tid] + part_a[3][tid]) / l;
     }
     __syncthreads();
+    const int j = tid % D;
+    const int h = tid / D;
+    const float* P = Pi_v + (int64_t)(p % H) * D * D + (int64_t)h * DJ * D + j;
+    float pv[DJ];
+#pragma unroll
+    for (int d = 0; d < DJ; ++d) pv[d] = P[(int64_t)d * D];
+    float o = 0.f;
+#pragma unroll
+    for (int d = 0; d < DJ; ++d) o = fmaf(pv[d], a[h * DJ + d], o);
+    po[h][j] = o;
+    __syncthreads();
     if (tid < D) {
-        const float* P = Pi_v + (int64_t)(p % H) * D * D;
-        float o = 0.f;
-#pragma unroll 16
-        for (int d = 0; d < D; ++d) o = fmaf(P[(int64_t)d * D + tid], a[d], o);
-        out[((int64_t)p * B + b) * D + tid] = o;
+        float r = 0.f;
+#pragma unroll
+        for (int k = 0; k < JP; ++k) r += po[k][tid];
+        out[((int64_t)p * B + b) * D + tid] = r;
     }
 }
 
@@ -472,6 +490,7 @@ struct Plan {
     int dblk;    // workgroups along the coordinates
     int nch;     // key chunks
     int chunk;   // keys per chunk
+    int nmax;    // chunk count before rounding (an upper bound on nch)
 };
 
 Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
@@ -495,14 +514,16 @@ Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
     const int64_t most = (S + cmin - 1) / cmin;
     if (n > most) n = most;
     if (n < 1) n = 1;
+    // split the coordinates (which repeats the weights' arithmetic in every
+    // block) only until there is about one workgroup per compute unit
+    const int ntfull = D / rows;
+    pl.dblk = 1;
+    while (pl.dblk < 4 && ntfull / (2 * pl.dblk) >= 1 && blocks * n * pl.dblk < kComputeUnits) pl.dblk *= 2;
+    pl.nt = ntfull / pl.dblk;
     const int64_t per = (S + n - 1) / n;
     pl.chunk = (int)((per + unit - 1) / unit * unit);
     pl.nch = (S + pl.chunk - 1) / pl.chunk;
-    // split the coordinates until there is about one workgroup per compute unit
-    const int ntfull = D / rows;
-    pl.dblk = 1;
-    while (pl.dblk < 4 && ntfull / (2 * pl.dblk) >= 1 && blocks * pl.nch * pl.dblk < kComputeUnits) pl.dblk *= 2;
-    pl.nt = ntfull / pl.dblk;
+    pl.nmax = (int)n;
     return pl;
 }
 
@@ -511,10 +532,10 @@ hipError_t launch_partial_q(const Plan& pl, const float* scores, ValueStreams v,
                             float scale, float* ws, int P, int B, int S, hipStream_t stream) {
     constexpr int NTF = D / Geo<MODE>::ROWS;
     const dim3 grid((unsigned)pl.nch, (unsigned)(pl.gy * pl.dblk), (unsigned)P);
-    const dim3 block(kWaves * 64);
-#define TQ_PARTIAL(NTV)                                                                                        \
-    hipLaunchKernelGGL((attend_partial_kernel<LAYOUT, BITS, D, MODE, QTW, NTV>), grid, block, 0, stream, scores, \
-                       v.idx, v.norm, codebook, C, scale, ws, B, S, pl.chunk, pl.nch)
+#define TQ_PARTIAL(NTV)                                                                                       \
+    hipLaunchKernelGGL((attend_partial_kernel<LAYOUT, BITS, D, MODE, QTW, NTV>), grid,                         \
+                       dim3(kWaves * 64), 0, stream, scores, v.idx, v.norm, codebook, C, scale, ws, \
+                       B, S, pl.chunk, pl.nch)
     constexpr int NT2 = NTF / 2 > 0 ? NTF / 2 : 1;
     constexpr int NT4 = NTF / 4 > 0 ? NTF / 4 : 1;
     if (pl.nt == NTF) TQ_PARTIAL(NTF);
@@ -557,7 +578,7 @@ hipError_t launch_attend_layout(const float* scores, ValueStreams v, const float
 
 // The unpacked layout reads the most bytes per key, so it has the shortest
 // chunks and the most of them: its count bounds every layout's.
-int attend_chunks(int P, int B, int S, int D) { return make_plan(P, B, S, D, 0, 0).nch; }
+int attend_chunks(int P, int B, int S, int D) { return make_plan(P, B, S, D, 0, 0).nmax; }
 
 bool attend_supported(int layout, int bits, int C, int D) {
     if (C < 1 || C > 8) return false;
