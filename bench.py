@@ -52,10 +52,11 @@ def parse():
                     help="decode (default, the quoted configuration); others for profiling")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
-    ap.add_argument("--path", default="score", choices=["score", "compress", "attend"],
+    ap.add_argument("--path", default="score", choices=["score", "compress", "attend", "mse"],
                     help="score (default): the scoring hot path; compress: the key compressor "
                          "(tq_compress_keys) on the workload's key set; attend: softmax and value "
-                         "aggregation (tq_attend) over the workload's scores and values")
+                         "aggregation (tq_attend) over the workload's scores and values; mse: the "
+                         "MSE-only variant (tq_query_transform_hadamard + tq_score_mse)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -478,6 +479,129 @@ def bench_attend(args, w, device) -> dict:
     return out
 
 
+def mse_bytes(w) -> int:
+    """Bytes tq_score_mse must move once: key indices and norms, A and the
+    codebook in, fp32 scores out."""
+    per_key = w.D + 4 if w.layout == "unpacked" else w.D * w.bits // 8 + 2
+    return w.P * w.S * per_key + w.P * w.B * w.D * 4 + w.C * 4 + w.P * w.B * w.S * 4
+
+
+def bench_mse(args, w, device) -> dict:
+    """One step = tq_query_transform_hadamard + tq_score_mse over the workload's
+    shape with MSE-only keys (its index layout and codebook size, one norm per
+    key, no signs). Per-kernel times from phased graph replays, as for the
+    scoring path."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+
+    bits = w.bits if w.layout == "packed" else 0
+    rng = np.random.default_rng([w.seed, 11])
+    signs = np.where(rng.integers(0, 2, size=(w.H, w.D)) == 1, 1.0, -1.0).astype(np.float32)
+    cb = synth.timing_codebook(w.seed, w.C, w.D)
+    idx, norm = synth.timing_value_streams(w.seed, w.P, w.S, w.D, w.C, w.layout, bits)
+    q = synth.queries(w.seed, w.P, w.B, w.D)
+    shared = {"signs": torch.from_numpy(signs).to(device), "cb": torch.from_numpy(cb).to(device)}
+    base = {"q": torch.from_numpy(q).to(device), "idx": torch.from_numpy(idx).to(device),
+            "norm": torch.from_numpy(norm).to(device)}
+    nbytes = mse_bytes(w)
+    nsets = max(2, min(64, math.ceil(RING_BYTES / nbytes)))
+    ring = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in base.items()}
+        s["keys"] = tq.Values(w.layout, s["idx"], s["norm"], bits)
+        s["A"] = torch.empty((w.P, w.B, w.D), dtype=torch.float32, device=device)
+        s["scores"] = torch.empty((w.P, w.B, w.S), dtype=torch.float32, device=device)
+        ring.append(s)
+
+    def transform(s):
+        tq.tq_query_transform_hadamard(s["q"], shared["signs"], s["A"])
+
+    def score(s):
+        tq.tq_score_mse(s["A"], s["keys"], shared["cb"], s["scores"])
+
+    for i in range(args.warmup):
+        transform(ring[i % nsets])
+        score(ring[i % nsets])
+    torch.cuda.synchronize()
+    steps = args.steps
+    chunks = [nsets] * (steps // nsets) + ([steps % nsets] if steps % nsets else [])
+    graphs = {}
+    for n in sorted(set(chunks)):
+        gt, gs = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gt):
+            for i in range(n):
+                transform(ring[i])
+        with torch.cuda.graph(gs):
+            for i in range(n):
+                score(ring[i])
+        graphs[n] = (gt, gs)
+    for gt, gs in graphs.values():
+        gt.replay()
+        gs.replay()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in chunks]
+    t0 = time.perf_counter()
+    for n, ev in zip(chunks, evs):
+        gt, gs = graphs[n]
+        ev[0].record()
+        gt.replay()
+        ev[1].record()
+        gs.replay()
+        ev[2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    qt_us = 1e3 * sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    sc_us = 1e3 * sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    ms_per_step = elapsed * 1e3 / steps
+    achieved = nbytes / (sc_us * 1e-6) / 1e9
+    log(f"mse: transform {qt_us:.2f} us, score {sc_us:.2f} us per launch, {achieved:.0f} GB/s algorithmic")
+    out = {
+        "metric": "query-key scores/sec, MSE-only keys (randomized Hadamard queries)",
+        "value": w.pairs / (ms_per_step * 1e-3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate",
+        "data": "synthetic: seeded random MSE codes and norms, N(0,1) queries, random Hadamard signs",
+        "config": {"workload": w.name, "path": "mse", "P": w.P, "H": w.H, "B": w.B, "S": w.S, "D": w.D, "C": w.C,
+                   "layout": w.layout, "bits": w.bits},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "score_mfma_kernel (MSE-only)",
+                     "bytes_per_launch": nbytes, "avg_launch_us": sc_us},
+        "tq_score_mse_us": sc_us,
+        "tq_query_transform_hadamard_us": qt_us,
+        "ring_sets": nsets,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import mse as om
+        from oracle import pack as opk
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        idx0 = idx[0] if w.layout == "unpacked" else opk.unpack_indices(idx[0], w.bits, w.D)
+        R = om.hadamard_rotation(signs[0].astype(np.float64))
+        n0 = norm[0].astype(np.float64)
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3:
+            t1 = time.perf_counter()
+            om.scores_mse_by_reconstruction(q[0], idx0, n0, R, cb)
+            times.append(time.perf_counter() - t1)
+        med = sorted(times)[len(times) // 2]
+        out["cpu_baseline"] = {"value": w.B * w.S / med, "unit": "scores/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"problem 0 (B={w.B}, S={w.S}, D={w.D}) scored by float64 explicit "
+                                         f"reconstruction, median of {len(times)} runs ({sum(times):.1f} s total)"}
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -501,6 +625,9 @@ def main() -> int:
         return 0
     if args.path == "attend":
         print(json.dumps(bench_attend(args, w, device)), flush=True)
+        return 0
+    if args.path == "mse":
+        print(json.dumps(bench_mse(args, w, device)), flush=True)
         return 0
     kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, args.kernel)
     log(f"workload {w.describe()} kernel {kname}")

@@ -11,6 +11,8 @@ functions keep the C names:
     tq_compress_keys(keys, Pi, S_mat, codebook, layout, bits) -> Keys
     tq_attend(scores, values, codebook, Pi_v, scale) -> out
     tq_attend_workspace_bytes(P, B, S, D)
+    tq_query_transform_hadamard(q, signs)      -> A
+    tq_score_mse(A, keys, codebook)            -> scores   (MSE-only keys: Values format)
     tq_score_kernel_name(layout, bits, C, P, B, S, D, kernel)
 
 Only argument marshalling happens here: shapes, dtypes, contiguity and device
@@ -30,7 +32,8 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform", "tq_score", "tq_score_with_kernel",
+    "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform_hadamard",
+    "tq_score_mse", "tq_query_transform", "tq_score", "tq_score_with_kernel",
     "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
     "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
 ]
@@ -99,6 +102,10 @@ def _load():
     lib.tq_attend.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp, vp, ctypes.c_size_t,
                               i32, i32, i32, i32, i32, vp]
     lib.tq_attend.restype = i32
+    lib.tq_query_transform_hadamard.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.tq_query_transform_hadamard.restype = i32
+    lib.tq_score_mse.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, i32, i32, i32, i32, vp]
+    lib.tq_score_mse.restype = i32
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     return lib
@@ -318,8 +325,9 @@ def tq_compress_keys(keys: torch.Tensor, Pi: torch.Tensor, S_mat: torch.Tensor, 
 
 @dataclass
 class Values:
-    """Compressed values of P problems with S values of D coordinates each
-    (v_s = norm_s * Pi_v^T codebook[idx_s]).
+    """MSE-only codes of P problems with S vectors of D coordinates each
+    (x_s = norm_s * Pi^T codebook[idx_s]): compressed values for tq_attend, and
+    keys for tq_score_mse.
 
     layout "unpacked": idx uint8 [P,S,D], norm float32 [P,S].
     layout "packed":   idx uint8 [P,S,D*bits/8] (LSB-first bitstream), norm float16 [P,S]; bits 2 or 3.
@@ -391,3 +399,45 @@ def tq_attend(scores: torch.Tensor, values: Values, codebook: torch.Tensor, Pi_v
                           float(scale), _ptr(out), _ptr(workspace), workspace.numel(), P, H, B, S, D, st),
            "tq_attend")
     return out.view(B, D) if squeeze else out.view(P, B, D)
+
+
+def tq_query_transform_hadamard(q: torch.Tensor, signs: torch.Tensor, A: torch.Tensor | None = None,
+                                stream=None) -> torch.Tensor:
+    """A = H (signs * q) / sqrt(D): q [P,B,D] or [B,D]; signs [H,D] or [D] of +-1."""
+    squeeze = q.dim() == 2
+    q3 = _as3(_gpu(q, "q", torch.float32))
+    sg = _gpu(signs, "signs", torch.float32)
+    sg2 = sg if sg.dim() == 2 else sg.unsqueeze(0)
+    P, B, D = q3.shape
+    H = sg2.shape[0]
+    if sg2.shape != (H, D):
+        raise ValueError(f"signs must be [H, {D}]")
+    if A is None:
+        A = torch.empty_like(q3)
+    _gpu(A, "A", torch.float32)
+    if A.numel() != q3.numel():
+        raise ValueError("A must have q's shape")
+    _check(_lib.tq_query_transform_hadamard(_ptr(q3), _ptr(sg2), _ptr(A), P, H, B, D, _stream(q.device, stream)),
+           "tq_query_transform_hadamard")
+    return A.view(B, D) if squeeze else A.view(P, B, D)
+
+
+def tq_score_mse(A: torch.Tensor, keys: Values, codebook: torch.Tensor, scores: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Scores [P,B,S] (or [B,S]) of transformed queries against MSE-only keys:
+    norm_s * sum_d A[b,d] codebook[idx[s,d]]."""
+    squeeze = A.dim() == 2
+    A3 = _as3(_gpu(A, "A", torch.float32))
+    _gpu(codebook, "codebook", torch.float32)
+    P, B, D = A3.shape
+    ck, Pk, S = keys._c(D)
+    if Pk != P:
+        raise ValueError(f"keys hold {Pk} problems, A holds {P}")
+    if scores is None:
+        scores = torch.empty((P, B, S), dtype=torch.float32, device=A.device)
+    _gpu(scores, "scores", torch.float32)
+    if scores.numel() != P * B * S:
+        raise ValueError("scores must hold P*B*S floats")
+    _check(_lib.tq_score_mse(_ptr(A3), ctypes.byref(ck), _ptr(codebook), codebook.numel(), _ptr(scores),
+                             P, B, S, D, _stream(A.device, stream)), "tq_score_mse")
+    return scores.view(B, S) if squeeze else scores.view(P, B, S)

@@ -204,6 +204,35 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
+int tq_query_transform_hadamard(const float* q, const float* signs, float* A, int P, int H, int B, int D,
+                                void* stream) {
+    if (P < 0 || H <= 0 || B < 0 || D <= 0 || P % H != 0) return TQ_ERR_ARG;
+    if (!tq::hadamard_supported(D)) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!q || !signs || !A) return TQ_ERR_ARG;
+    if (!fits(P, B, D) || (int64_t)P * B > (int64_t)1 << 30) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(signs) || !aligned16(A)) return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_query_transform_hadamard(q, signs, A, P, H, B, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_score_mse(const float* A, const tq_mse_codes* keys, const float* codebook, int C, float* scores, int P,
+                 int B, int S, int D, void* stream) {
+    if (!keys || P < 0 || B < 0 || S < 0 || D <= 0) return TQ_ERR_ARG;
+    if (keys->layout != TQ_UNPACKED && keys->layout != TQ_PACKED) return TQ_ERR_ARG;
+    const int bits = keys->layout == TQ_PACKED ? keys->bits : 0;
+    if (keys->layout == TQ_PACKED && ((bits != 2 && bits != 3) || C != (1 << bits))) return TQ_ERR_UNSUPPORTED;
+    if (!tq::score_mse_supported(keys->layout, bits, C, D)) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0 || S == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!A || !codebook || !scores || !keys->idx || !keys->norm) return TQ_ERR_ARG;
+    if (S >= kMfmaMaxKeys || P > 65535 || B > 262144 || !fits(P, B, S) || !fits(P, S, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(A) || !aligned16(codebook) || !aligned16(scores) || !aligned16(keys->idx) || !aligned16(keys->norm))
+        return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_score_mse(A, static_cast<const uint8_t*>(keys->idx), keys->norm, keys->layout,
+                                              bits, codebook, C, scores, P, B, S, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                     int P, int S, int D, void* stream) {
     if (P < 0 || S < 0) return TQ_ERR_ARG;

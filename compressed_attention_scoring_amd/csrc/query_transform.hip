@@ -189,7 +189,77 @@ __global__ __launch_bounds__(256) void query_transform_mfma_kernel(
     }
 }
 
+// Randomized Hadamard query transform A = H (signs * q) with H the orthonormal
+// Walsh-Hadamard matrix in Sylvester order ("TurboQuant: Rotate-then-Quantize
+// KV Caches at 3 Bits", section 2: y = H D x, O(d log d)). One wavefront per
+// query; lane l holds coordinates E*l .. E*l+E-1 (E = D/64, at least 1). The
+// butterfly at distance h pairs coordinates i and i+h (bit h of i clear):
+// (x_i + x_(i+h), x_i - x_(i+h)); distances below E stay inside a lane, larger
+// ones pair lane l with lane l ^ (h/E). The 1/sqrt(D) normalisation comes last.
+template <int D>
+__global__ __launch_bounds__(256) void hadamard_query_kernel(const float* __restrict__ q,
+                                                             const float* __restrict__ signs,
+                                                             float* __restrict__ A, int H, int B, int NQ) {
+    constexpr int E = D >= 64 ? D / 64 : 1;
+    const int lane = threadIdx.x & 63;
+    const int qi = blockIdx.x * 4 + (threadIdx.x >> 6);     // query index over all problems
+    if (qi >= NQ) return;                                     // whole wavefronts leave together
+    const int p = qi / B;
+    const float* src = q + (int64_t)qi * D;
+    const float* sg = signs + (int64_t)(p % H) * D;
+    const bool active = lane * E < D;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = min(lane * E + e, D - 1);
+        x[e] = active ? src[i] * sg[i] : 0.f;
+    }
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & h) == 0) {
+                const float a = x[e], b = x[e + h];
+                x[e] = a + b;
+                x[e + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int h = E; h < D; h <<= 1) {
+        const int m = h / E;                                  // lane distance
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float other = __shfl_xor(x[e], m);
+            x[e] = upper ? other - x[e] : x[e] + other;
+        }
+    }
+    const float norm = 1.0f / sqrtf((float)D);
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) A[(int64_t)qi * D + lane * E + e] = x[e] * norm;
+    }
+}
+
 }  // namespace
+
+bool hadamard_supported(int D) { return D >= 1 && D <= 1024 && (D & (D - 1)) == 0; }
+
+hipError_t launch_query_transform_hadamard(const float* q, const float* signs, float* A, int P, int H, int B,
+                                           int D, hipStream_t stream) {
+    const int nq = P * B;
+    const dim3 grid((unsigned)((nq + 3) / 4)), block(256);
+    switch (D) {
+#define TQ_HADAMARD(DV) \
+    case DV: hipLaunchKernelGGL(hadamard_query_kernel<DV>, grid, block, 0, stream, q, signs, A, H, B, nq); break;
+        TQ_HADAMARD(1) TQ_HADAMARD(2) TQ_HADAMARD(4) TQ_HADAMARD(8) TQ_HADAMARD(16) TQ_HADAMARD(32)
+        TQ_HADAMARD(64) TQ_HADAMARD(128) TQ_HADAMARD(256) TQ_HADAMARD(512) TQ_HADAMARD(1024)
+#undef TQ_HADAMARD
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_query_transform(const float* q, const float* Pi, const float* S_mat,
                                   float* A, float* T, int P, int H, int B, int D,

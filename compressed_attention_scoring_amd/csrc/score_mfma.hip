@@ -431,7 +431,7 @@ struct TileCodes {
 
 // Key-side operands of k-step j: codebook hi and lo parts looked up by index,
 // and signs as f16 +-1.
-template <int LAYOUT, int BITS, int NI, int NS>
+template <int LAYOUT, int BITS, int NI, int NS, bool QJL = true>
 __device__ __forceinline__ void key_operands(const TileCodes<NI, NS>& c, int j, const uint32_t (&tab_hi)[4],
                                              const uint32_t (&tab_lo)[4], Op8& chi, Op8& clo, Op8& sg) {
     using F = Fmt<LAYOUT, BITS>;
@@ -441,7 +441,7 @@ __device__ __forceinline__ void key_operands(const TileCodes<NI, NS>& c, int j, 
     lut4(x1, tab_hi, chi.u[2], chi.u[3]);
     lut4(x0, tab_lo, clo.u[0], clo.u[1]);
     lut4(x1, tab_lo, clo.u[2], clo.u[3]);
-    F::template signs<NS>(c.sw, j, sg.u);
+    if constexpr (QJL) F::template signs<NS>(c.sw, j, sg.u);
 }
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
@@ -450,8 +450,9 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kValuPerMfma = 7;
 
-// Segment m (0 or 1) of a key: coordinates [m*D/2, (m+1)*D/2).
-template <int LAYOUT, int BITS, int D>
+// Segment m (0 or 1) of a key: coordinates [m*D/2, (m+1)*D/2). Without QJL
+// (MSE-only keys) there is no sign stream and `gamma` is the key's norm.
+template <int LAYOUT, int BITS, int D, bool QJL = true>
 __device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
                                                     Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
                                           const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
@@ -464,12 +465,13 @@ __device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template 
     constexpr int IDX_SEG = IDX_ROW / 2;
     constexpr int SIGN_SEG = SIGN_ROW / 2;
     load_dwords<NI, align_of_seg(IDX_ROW, IDX_SEG)>(idx + key * IDX_ROW + m * IDX_SEG, c.iw);
-    load_dwords<NS, align_of_seg(SIGN_ROW, SIGN_SEG)>(sign + key * SIGN_ROW + m * SIGN_SEG, c.sw);
+    if constexpr (QJL) load_dwords<NS, align_of_seg(SIGN_ROW, SIGN_SEG)>(sign + key * SIGN_ROW + m * SIGN_SEG, c.sw);
     if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
     else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
 }
 
-template <int LAYOUT, int BITS, int D, int MT>
+// QJL = false scores MSE-only keys: scores = norm_s * M (no T, no signs).
+template <int LAYOUT, int BITS, int D, int MT, bool QJL>
 __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
@@ -526,9 +528,13 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 #pragma unroll
         for (int k = 0; k < SEG; k += 4) {
             const float4 va = *reinterpret_cast<const float4*>(Ap + (int64_t)rowc * D + pl * SEG + k);
-            const float4 vt = *reinterpret_cast<const float4*>(Tp + (int64_t)rowc * D + pl * SEG + k);
             a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
-            t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+            if constexpr (QJL) {
+                const float4 vt = *reinterpret_cast<const float4*>(Tp + (int64_t)rowc * D + pl * SEG + k);
+                t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+            } else {
+                t[k] = t[k + 1] = t[k + 2] = t[k + 3] = 0.f;
+            }
         }
         // The first tile's codes are requested right behind the first rows of A
         // and T: vector loads retire in issue order, so converting A and T waits
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         if (r0 == 0) {
             asm volatile("" ::: "memory");
             const int s = min(min(tile, ntiles - 1) * kTileKeys + col, S - 1);
-            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
+            load_tile<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma, key0 + s, g);
             asm volatile("" ::: "memory");
             // codebook tables; their loads come after the vector loads above so
             // their latency is not paid first
@@ -578,11 +584,13 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
                 uint8_t* base = lane_base + (j * 4) * BLOCK + e * 2;
                 *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = hi;
                 *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = lo;
-                qjl_slot16<LAYOUT>(blk16, k, j, e);
-                split_f16(t[k] * sT, hi, lo);
-                base = lane_base + (j * 4) * BLOCK + e * 2;
-                *reinterpret_cast<uint16_t*>(base + 2 * BLOCK) = hi;
-                *reinterpret_cast<uint16_t*>(base + 3 * BLOCK) = lo;
+                if constexpr (QJL) {
+                    qjl_slot16<LAYOUT>(blk16, k, j, e);
+                    split_f16(t[k] * sT, hi, lo);
+                    base = lane_base + (j * 4) * BLOCK + e * 2;
+                    *reinterpret_cast<uint16_t*>(base + 2 * BLOCK) = hi;
+                    *reinterpret_cast<uint16_t*>(base + 3 * BLOCK) = lo;
+                }
             }
         }
     }
@@ -602,7 +610,9 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             for (int v = 0; v < 16; ++v) { accM[mt][v] = 0.f; accR[mt][v] = 0.f; }
         }
         Op8 chi[2], clo[2], sg[2];
-        key_operands<LAYOUT, BITS, NI, NS>(c, 0, tab_hi, tab_lo, chi[0], clo[0], sg[0]);
+        key_operands<LAYOUT, BITS, NI, NS, QJL>(c, 0, tab_hi, tab_lo, chi[0], clo[0], sg[0]);
+        constexpr int NOPS = QJL ? 4 : 2;      // LDS operand blocks read per 32-query tile and k-step
+        constexpr int NMFMA = QJL ? 5 : 3;     // products per 32-query tile and k-step
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             const int u = j & 1;
@@ -612,22 +622,27 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
                 const uint8_t* base = my_ops + ((mt * KS + j) * 4) * BLOCK;
                 *reinterpret_cast<uint4*>(ahi[mt].u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
                 *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
-                *reinterpret_cast<uint4*>(thi[mt].u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
-                *reinterpret_cast<uint4*>(tlo[mt].u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
+                if constexpr (QJL) {
+                    *reinterpret_cast<uint4*>(thi[mt].u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
+                    *reinterpret_cast<uint4*>(tlo[mt].u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
+                }
             }
-            if (j + 1 < KS) key_operands<LAYOUT, BITS, NI, NS>(c, j + 1, tab_hi, tab_lo, chi[u ^ 1], clo[u ^ 1], sg[u ^ 1]);
+            if (j + 1 < KS)
+                key_operands<LAYOUT, BITS, NI, NS, QJL>(c, j + 1, tab_hi, tab_lo, chi[u ^ 1], clo[u ^ 1], sg[u ^ 1]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, chi[u].h, accM[mt], 0, 0, 0);
-                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[mt].h, sg[u].h, accR[mt], 0, 0, 0);
+                if constexpr (QJL)
+                    accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[mt].h, sg[u].h, accR[mt], 0, 0, 0);
                 accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[mt].h, chi[u].h, accM[mt], 0, 0, 0);
-                accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[mt].h, sg[u].h, accR[mt], 0, 0, 0);
+                if constexpr (QJL)
+                    accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[mt].h, sg[u].h, accR[mt], 0, 0, 0);
                 accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, clo[u].h, accM[mt], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * MT, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NOPS * MT, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
 #pragma unroll
-            for (int i = 0; i < 5 * MT; ++i) {
+            for (int i = 0; i < NMFMA * MT; ++i) {
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(kSchedValu, MT == 1 ? 5 : 1, 0);
             }
@@ -641,7 +656,10 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float2 k = rowk[mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3)];
-                store_score(out_r, lo + row_offset(v, S), fmaf(k.y * c.gam, accR[mt][v], accM[mt][v] * k.x));
+                if constexpr (QJL)
+                    store_score(out_r, lo + row_offset(v, S), fmaf(k.y * c.gam, accR[mt][v], accM[mt][v] * k.x));
+                else
+                    store_score(out_r, lo + row_offset(v, S), (accM[mt][v] * k.x) * c.gam);
             }
         }
     };
@@ -651,13 +669,13 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     if (tile < ntiles) {
         TileCodes<NI, NS> nxt;
         while (true) {
-            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma,
-                                       key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+            load_tile<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
+                                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
             tile_scores(cur, tile);
             tile += stride;
             if (tile >= ntiles) break;
-            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma,
-                                       key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+            load_tile<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma,
+                                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
             tile_scores(nxt, tile);
             tile += stride;
             if (tile >= ntiles) break;
@@ -1200,7 +1218,7 @@ int mt_for(int B, int D) {
     return 1;
 }
 
-template <int LAYOUT, int BITS, int D, int MT>
+template <int LAYOUT, int BITS, int D, int MT, bool QJL>
 hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                      float* scores, int P, int B, int S, hipStream_t stream) {
     const int groups_y = (B + MT * 32 - 1) / (MT * 32);
@@ -1219,7 +1237,7 @@ hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* 
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT>), dim3((unsigned)gx, groups_y, P),
+    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT, QJL>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();
@@ -1342,32 +1360,32 @@ hipError_t launch_qs_layout(const float* A, const float* T, KeyStreams k, const 
     return hipErrorInvalidValue;
 }
 
-template <int LAYOUT, int BITS, int D>
+template <int LAYOUT, int BITS, int D, bool QJL>
 hipError_t launch_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                     float* scores, int P, int B, int S, hipStream_t stream) {
     switch (mt_for(B, D)) {
         case 4:
             if constexpr (D <= 128)
-                return launch_mt<LAYOUT, BITS, D, 4>(A, T, k, codebook, C, scores, P, B, S, stream);
+                return launch_mt<LAYOUT, BITS, D, 4, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
             [[fallthrough]];
         case 2:
-            return launch_mt<LAYOUT, BITS, D, 2>(A, T, k, codebook, C, scores, P, B, S, stream);
+            return launch_mt<LAYOUT, BITS, D, 2, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
         default:
-            return launch_mt<LAYOUT, BITS, D, 1>(A, T, k, codebook, C, scores, P, B, S, stream);
+            return launch_mt<LAYOUT, BITS, D, 1, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
     }
 }
 
-template <int LAYOUT, int BITS>
+template <int LAYOUT, int BITS, bool QJL = true>
 hipError_t launch_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                          int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
     switch (D) {
         case 32:
             if constexpr (LAYOUT == 0)
-                return launch_d<LAYOUT, BITS, 32>(A, T, k, codebook, C, scores, P, B, S, stream);
+                return launch_d<LAYOUT, BITS, 32, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
             break;
-        case 64: return launch_d<LAYOUT, BITS, 64>(A, T, k, codebook, C, scores, P, B, S, stream);
-        case 128: return launch_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
-        case 256: return launch_d<LAYOUT, BITS, 256>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 64: return launch_d<LAYOUT, BITS, 64, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 128: return launch_d<LAYOUT, BITS, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 256: return launch_d<LAYOUT, BITS, 256, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
         default: break;
     }
     return hipErrorInvalidValue;
@@ -1463,6 +1481,18 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
     if (layout == 0) return launch_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
     if (bits == 2) return launch_layout<1, 2>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
     return launch_layout<1, 3>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+}
+
+bool score_mse_supported(int layout, int bits, int C, int D) { return lds_supported(layout, bits, C, D); }
+
+hipError_t launch_score_mse(const float* A, const uint8_t* idx, const void* norm, int layout, int bits,
+                            const float* codebook, int C, float* scores, int P, int B, int S, int D,
+                            hipStream_t stream) {
+    if (!score_mse_supported(layout, bits, C, D)) return hipErrorInvalidValue;
+    const KeyStreams k{idx, nullptr, norm};
+    if (layout == 0) return launch_layout<0, 0, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+    if (bits == 2) return launch_layout<1, 2, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+    return launch_layout<1, 3, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
 }
 
 }  // namespace tq

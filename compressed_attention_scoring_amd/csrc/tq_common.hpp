@@ -74,6 +74,18 @@ hipError_t launch_attend(const float* scores, ValueStreams v, int layout, int bi
                          const float* Pi_v, float scale, float* out, float* ws, int P, int H, int B, int S, int D,
                          hipStream_t stream);
 
+// MSE-only keys (indices as in KeyStreams, one norm per key, no signs):
+// scores = norm_s * sum_d A[b,d] codebook[idx[s,d]], on the LDS-staged kernel.
+bool score_mse_supported(int layout, int bits, int C, int D);
+hipError_t launch_score_mse(const float* A, const uint8_t* idx, const void* norm, int layout, int bits,
+                            const float* codebook, int C, float* scores, int P, int B, int S, int D,
+                            hipStream_t stream);
+
+// A = H (signs * q) / sqrt(D) for D a power of two up to 1024.
+bool hadamard_supported(int D);
+hipError_t launch_query_transform_hadamard(const float* q, const float* signs, float* A, int P, int H, int B,
+                                           int D, hipStream_t stream);
+
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                          int P, int S, int D, hipStream_t stream);

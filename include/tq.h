@@ -214,22 +214,26 @@ int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat,
                      int P, int H, int S, int D, void* stream);
 
 /*
- * Compressed values of P problems, S values each, D coordinates per value:
- * the MSE quantizer of "TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits"
- * (section 3, with the norm kept separately as its value cache does in
- * section 8): v_s = norm[s] * Pi_v^T codebook[idx[s, :]].
+ * MSE-only codes of P problems, S vectors each, D coordinates per vector: the
+ * MSE quantizer of "TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits"
+ * (section 3, the norm kept separately as its value cache does in section 8):
+ * x_s = norm[s] * Pi^T codebook[idx[s, :]]. The format of compressed values
+ * (tq_attend) and of keys in the MSE-only scoring variant (tq_score_mse).
  *
  * layout == TQ_UNPACKED: idx uint8 [P, S, D] (< C), norm float32 [P, S]; bits ignored.
  * layout == TQ_PACKED:   idx uint8 [P, S, D*bits/8] as the packed key indices
- *                        above (LSB-first bitstream per value), norm float16
+ *                        above (LSB-first bitstream per vector), norm float16
  *                        [P, S]; bits 2 or 3, C == 2^bits.
  */
-typedef struct tq_values {
+typedef struct tq_mse_codes {
     int32_t layout;
     int32_t bits;
     const void* idx;
     const void* norm;
-} tq_values;
+} tq_mse_codes;
+
+/* compressed values */
+typedef tq_mse_codes tq_values;
 
 /*
  * tq_attend_workspace_bytes: bytes of the workspace tq_attend needs for this
@@ -269,6 +273,46 @@ size_t tq_attend_workspace_bytes(int P, int B, int S, int D);
 int tq_attend(const float* scores, const tq_values* values, const float* codebook, int C,
               const float* Pi_v, float scale, float* out, void* workspace, size_t workspace_bytes,
               int P, int H, int B, int S, int D, void* stream);
+
+/*
+ * tq_query_transform_hadamard: A = H D q for every query, the randomized
+ * Hadamard rotation ("TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits",
+ * section 2): D = diag(signs) of the query's head, H the orthonormal
+ * Walsh-Hadamard matrix in Sylvester order (H[i][j] = (-1)^popcount(i & j) /
+ * sqrt(D)). O(D log D) per query instead of the dense product.
+ *
+ *   q      float32 [P, B, D]
+ *   signs  float32 [H, D]      +1 or -1 (problem p uses head p % H)
+ *   A      float32 [P, B, D]   output
+ *
+ * D a power of two, 1 <= D <= TQ_MAX_D (else TQ_ERR_UNSUPPORTED). fp32
+ * arithmetic (log2(D) butterfly stages, then the 1/sqrt(D) scale).
+ */
+int tq_query_transform_hadamard(const float* q, const float* signs, float* A,
+                                int P, int H, int B, int D, void* stream);
+
+/*
+ * tq_score_mse: raw scores against MSE-only keys, the variant that drops the
+ * QJL term ("TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits", sections 3
+ * and 6: the MSE quantizer with a stored norm, used for attention with norm
+ * correction):
+ *
+ *   scores[p,b,s] = norm[p,s] * sum_d A[p,b,d] * codebook[idx[p,s,d]]
+ *
+ * with A = Pi q (tq_query_transform's A, or tq_query_transform_hadamard). With
+ * norm correction the stored norm is ||k|| / ||codebook[idx]||, so the same
+ * formula serves both.
+ *
+ *   A         float32 [P, B, D]
+ *   keys      MSE-only codes (struct above; host pointer, device pointers inside)
+ *   codebook  float32 [C], 1 <= C <= 8 (packed: C == 2^bits)
+ *   scores    float32 [P, B, S]   output
+ *
+ * D in {64, 128, 256} (also 32 unpacked), S < 2^24 (else TQ_ERR_UNSUPPORTED).
+ * Result within 1e-4 * (1 + |exact|) of the exact value for the given inputs.
+ */
+int tq_score_mse(const float* A, const tq_mse_codes* keys, const float* codebook, int C,
+                 float* scores, int P, int B, int S, int D, void* stream);
 
 /* tq_status_string: static description of a status code. */
 const char* tq_status_string(int status);

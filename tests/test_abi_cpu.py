@@ -12,6 +12,7 @@ import compressed_attention_scoring_amd as tq
 EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
+    "tq_query_transform_hadamard", "tq_score_mse",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -183,3 +184,31 @@ def test_attend_rejects_bad_arguments():
     assert f(16, vals(idx=24), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ALIGN
     assert f(None, vals(idx=None, norm=None), None, 4, None, 1.0, None, None, 0, 1, 1, 0, 8, 128, None) == OK
     assert f(None, vals(idx=None, norm=None), None, 4, None, 1.0, None, None, 0, 0, 1, 4, 8, 128, None) == OK
+
+
+def test_hadamard_transform_rejects_bad_arguments():
+    f = tq._lib.tq_query_transform_hadamard
+    assert f(None, 16, 16, 1, 1, 2, 128, None) == ARG
+    assert f(16, 16, 16, 3, 2, 2, 128, None) == ARG        # P % H != 0
+    assert f(16, 16, 16, 1, 0, 2, 128, None) == ARG
+    assert f(16, 16, 16, 1, 1, 2, 96, None) == UNSUP       # not a power of two
+    assert f(16, 16, 16, 1, 1, 2, 2048, None) == UNSUP
+    assert f(20, 16, 16, 1, 1, 2, 128, None) == ALIGN
+    assert f(None, None, None, 0, 1, 2, 128, None) == OK
+    assert f(None, None, None, 1, 1, 0, 128, None) == OK
+
+
+def test_score_mse_rejects_bad_arguments():
+    f = tq._lib.tq_score_mse
+    keys = lambda layout=0, bits=0, idx=16, norm=16: ctypes.byref(tq._CValues(layout, bits, idx, norm))
+    assert f(16, None, 16, 4, 16, 1, 4, 8, 128, None) == ARG
+    assert f(16, keys(layout=3), 16, 4, 16, 1, 4, 8, 128, None) == ARG
+    assert f(None, keys(), 16, 4, 16, 1, 4, 8, 128, None) == ARG
+    assert f(16, keys(norm=None), 16, 4, 16, 1, 4, 8, 128, None) == ARG
+    assert f(16, keys(), 16, 4, 16, 1, 4, -1, 128, None) == ARG
+    assert f(16, keys(), 16, 16, 16, 1, 4, 8, 128, None) == UNSUP          # C > 8
+    assert f(16, keys(), 16, 4, 16, 1, 4, 8, 96, None) == UNSUP            # D
+    assert f(16, keys(layout=1, bits=3), 16, 4, 16, 1, 4, 8, 128, None) == UNSUP
+    assert f(16, keys(), 16, 4, 16, 1, 4, 1 << 24, 128, None) == UNSUP
+    assert f(16, keys(idx=20), 16, 4, 16, 1, 4, 8, 128, None) == ALIGN
+    assert f(None, keys(idx=None, norm=None), None, 4, None, 1, 4, 0, 128, None) == OK
