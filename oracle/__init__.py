@@ -15,9 +15,10 @@ Modules
   workload         seeded end-to-end input sets for the named workloads
   attend           decode output over compressed values: softmax and rotated-domain sum
   mse              MSE-only keys (stored norm, norm correction), randomized Hadamard rotation
+  split            the outlier split: two MSE instances per head over disjoint channel sets
 
 Every function is pinned by tests under ``tests/`` against values the pages
 print, closed forms, library routines or brute force; see each module.
 """
 
-from . import attend, codebook, compress, mse, pack, query_transform, score, workload  # noqa: F401
+from . import attend, codebook, compress, mse, pack, query_transform, score, split, workload  # noqa: F401

@@ -1,0 +1,116 @@
+"""Pins for oracle.split (the outlier split: two instances per head)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import mse as om
+from oracle import split as osp
+from oracle.codebook import codebook_fp32
+
+
+def test_bit_budgets_of_the_page():
+    # 32 hot channels at 3 bits and 96 at 2 give 2.5 bits per channel (section 7);
+    # half the channels at 4 bits and half at 3 give 3.5
+    assert osp.bits_per_channel(32, 3, 96, 2) == 2.5
+    assert osp.bits_per_channel(64, 4, 64, 3) == 3.5
+
+
+def test_channel_permutation():
+    perm = osp.channel_permutation(8, [5, 1, 5])
+    np.testing.assert_array_equal(perm, [1, 5, 0, 2, 3, 4, 6, 7])
+    np.testing.assert_array_equal(np.sort(osp.channel_permutation(128, [3, 17, 64, 101])), np.arange(128))
+    with pytest.raises(ValueError):
+        osp.channel_permutation(8, [8])
+
+
+def test_hot_channels_found_on_outlier_keys():
+    k = synth.unit_keys(np.random.default_rng(1), 2000, 128, "outlier")
+    hot = osp.choose_hot_channels(k, 32)
+    assert hot.size == 32 and set(synth.OUTLIER_CHANNELS) <= set(hot.tolist())
+    # on isotropic keys nothing stands out, but the count and order hold
+    hot_u = osp.choose_hot_channels(synth.unit_keys(np.random.default_rng(2), 500, 128, "uniform"), 32)
+    assert hot_u.size == 32 and np.all(np.diff(hot_u) > 0)
+
+
+def setup(seed=3, D=128, d_hi=32, C_hi=8, C_lo=4, S=60, nc=False):
+    rng = np.random.default_rng(seed)
+    k = synth.unit_keys(rng, S, D, "outlier") * rng.uniform(0.5, 2.0, (S, 1))
+    perm = osp.channel_permutation(D, osp.choose_hot_channels(k, d_hi))
+    Pi_hi = synth.haar_rotation(rng, d_hi).astype(np.float64)
+    Pi_lo = synth.haar_rotation(rng, D - d_hi).astype(np.float64)
+    cb_hi = codebook_fp32(d_hi, C_hi).astype(np.float64)
+    cb_lo = codebook_fp32(D - d_hi, C_lo).astype(np.float64)
+    codes = osp.compress_split(k, perm, d_hi, Pi_hi, Pi_lo, cb_hi, cb_lo, nc)
+    return k, perm, Pi_hi, Pi_lo, cb_hi, cb_lo, codes
+
+
+@pytest.mark.parametrize("nc", [False, True])
+def test_split_scores_equal_reconstruction(nc):
+    k, perm, Pi_hi, Pi_lo, cb_hi, cb_lo, (ih, rh, il, rl) = setup(nc=nc)
+    q = np.random.default_rng(4).standard_normal((5, 128))
+    A_hi, A_lo = osp.query_transform_split(q, perm, 32, Pi_hi, Pi_lo)
+    np.testing.assert_allclose(
+        osp.scores_split_from_transformed(A_hi, ih, rh, cb_hi, A_lo, il, rl, cb_lo),
+        osp.scores_split_by_reconstruction(q, perm, 32, ih, rh, Pi_hi, cb_hi, il, rl, Pi_lo, cb_lo),
+        rtol=0, atol=1e-12)
+
+
+def test_instance_norms_add_in_quadrature():
+    k, perm, *_, (ih, rh, il, rl) = setup()
+    np.testing.assert_allclose(rh ** 2 + rl ** 2, np.sum(k * k, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(rh, np.linalg.norm(k[:, perm[:32]], axis=1), rtol=1e-14)
+
+
+def test_each_instance_is_the_mse_quantizer_of_its_channels():
+    k, perm, Pi_hi, Pi_lo, cb_hi, cb_lo, (ih, rh, il, rl) = setup()
+    sub = k[:, perm[32:]]
+    unit = sub / np.linalg.norm(sub, axis=1, keepdims=True)
+    y = unit @ Pi_lo.T
+    np.testing.assert_array_equal(il, np.argmin(np.abs(y[..., None] - cb_lo), axis=-1))
+    k_hat = osp.dequantize_split(perm, 32, ih, rh, Pi_hi, cb_hi, il, rl, Pi_lo, cb_lo)
+    np.testing.assert_allclose(k_hat[:, perm[:32]], om.dequantize_mse_keys(ih, rh, Pi_hi, cb_hi), atol=0)
+
+
+def test_empty_hot_set_reduces_to_one_mse_instance():
+    rng = np.random.default_rng(5)
+    D = 64
+    k = rng.standard_normal((30, D))
+    perm = osp.channel_permutation(D, [])
+    np.testing.assert_array_equal(perm, np.arange(D))
+    Pi = synth.haar_rotation(rng, D).astype(np.float64)
+    cb = codebook_fp32(D, 4).astype(np.float64)
+    ih, rh, il, rl = osp.compress_split(k, perm, 0, np.zeros((0, 0)), Pi, np.zeros(1), cb)
+    idx, rho = om.compress_mse(k, Pi, cb)
+    np.testing.assert_array_equal(il, idx)
+    np.testing.assert_allclose(rl, rho, rtol=1e-15)
+    q = rng.standard_normal((3, D))
+    np.testing.assert_allclose(
+        osp.scores_split_by_reconstruction(q, perm, 0, ih, rh, np.zeros((0, 0)), np.zeros(1), il, rl, Pi, cb),
+        om.scores_mse_by_reconstruction(q, idx, rho, Pi, cb), atol=1e-12)
+
+
+def test_split_error_sits_between_the_uniform_widths():
+    """On keys with hot channels, 2.5 bits split (3 bits on the 32 hottest) lands
+    between uniform 2-bit and uniform 3-bit MSE quantization (relative error of
+    the reconstruction)."""
+    rng = np.random.default_rng(6)
+    D = 128
+    k = synth.unit_keys(rng, 3000, D, "outlier")
+    perm = osp.channel_permutation(D, osp.choose_hot_channels(k, 32))
+    Pi_hi = synth.haar_rotation(rng, 32).astype(np.float64)
+    Pi_lo = synth.haar_rotation(rng, 96).astype(np.float64)
+    codes = osp.compress_split(k, perm, 32, Pi_hi, Pi_lo, codebook_fp32(32, 8).astype(np.float64),
+                               codebook_fp32(96, 4).astype(np.float64))
+    k_split = osp.dequantize_split(perm, 32, codes[0], codes[1], Pi_hi, codebook_fp32(32, 8).astype(np.float64),
+                                   codes[2], codes[3], Pi_lo, codebook_fp32(96, 4).astype(np.float64))
+    Pi = synth.haar_rotation(rng, D).astype(np.float64)
+    err = {}
+    for C in (4, 8):
+        cb = codebook_fp32(D, C).astype(np.float64)
+        idx, rho = om.compress_mse(k, Pi, cb)
+        err[C] = np.mean(np.sum((om.dequantize_mse_keys(idx, rho, Pi, cb) - k) ** 2, axis=1))
+    e_split = np.mean(np.sum((k_split - k) ** 2, axis=1))
+    assert err[8] < e_split < err[4]
