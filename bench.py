@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "query-key scores/sec + achieved HBM GB/s, B=32 S=32768 D=128 3-bit keys"
 HBM_PEAK_GBS = 8000.0
 FP64_MATRIX_PEAK_TFLOPS = 78.6
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 RING_BYTES = 512 * 1024 * 1024
 
 
@@ -52,11 +53,13 @@ def parse():
                     help="decode (default, the quoted configuration); others for profiling")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
-    ap.add_argument("--path", default="score", choices=["score", "compress", "attend", "mse"],
+    ap.add_argument("--path", default="score", choices=["score", "compress", "attend", "mse", "split"],
                     help="score (default): the scoring hot path; compress: the key compressor "
                          "(tq_compress_keys) on the workload's key set; attend: softmax and value "
                          "aggregation (tq_attend) over the workload's scores and values; mse: the "
-                         "MSE-only variant (tq_query_transform_hadamard + tq_score_mse)")
+                         "MSE-only variant (tq_query_transform_hadamard + tq_score_mse); split: the "
+                         "outlier split, 32 hot channels at 3 bits + the rest at 2 (tq_query_transform_split "
+                         "+ tq_score_split)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -602,6 +605,138 @@ def bench_mse(args, w, device) -> dict:
     return out
 
 
+def bench_split(args, w, device) -> dict:
+    """One step = tq_query_transform_split + tq_score_split over the workload's
+    shape (P, B, S, D) with outlier-split keys: the 32 hot channels at 3 bits
+    (C=8) and the other D-32 at 2 bits (C=4), both packed with fp16 norms."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+
+    d_hi, d_lo = 32, w.D - 32
+    rng = np.random.default_rng([w.seed, 21])
+    perm = np.concatenate([np.arange(0, w.D, w.D // d_hi), np.setdiff1d(np.arange(w.D), np.arange(0, w.D, w.D // d_hi))])
+    perm = perm.astype(np.int32)
+    Pi_hi = np.stack([synth.haar_rotation(rng, d_hi) for _ in range(w.H)])
+    Pi_lo = np.stack([synth.haar_rotation(rng, d_lo) for _ in range(w.H)])
+    cb_hi = synth.timing_codebook(w.seed, 8, d_hi)
+    cb_lo = synth.timing_codebook(w.seed + 1, 4, d_lo)
+    ih, nh = synth.timing_value_streams(w.seed, w.P, w.S, d_hi, 8, "packed", 3)
+    il, nl = synth.timing_value_streams(w.seed + 1, w.P, w.S, d_lo, 4, "packed", 2)
+    q = synth.queries(w.seed, w.P, w.B, w.D)
+    shared = {k: torch.from_numpy(v).to(device) for k, v in
+              {"perm": perm, "Pi_hi": Pi_hi, "Pi_lo": Pi_lo, "cb_hi": cb_hi, "cb_lo": cb_lo}.items()}
+    base = {k: torch.from_numpy(v).to(device) for k, v in {"q": q, "ih": ih, "nh": nh, "il": il, "nl": nl}.items()}
+    nbytes = (w.P * w.S * (d_hi * 3 // 8 + 2 + d_lo * 2 // 8 + 2) + w.P * w.B * w.D * 4 + 12 * 4
+              + w.P * w.B * w.S * 4)
+    flops = 2 * w.P * w.B * w.S * w.D
+    nsets = max(2, min(64, math.ceil(RING_BYTES / nbytes)))
+    ring = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in base.items()}
+        s["keys"] = tq.SplitKeys(tq.Values("packed", s["ih"], s["nh"], 3), tq.Values("packed", s["il"], s["nl"], 2))
+        s["A"] = None
+        s["scores"] = torch.empty((w.P, w.B, w.S), dtype=torch.float32, device=device)
+        ring.append(s)
+
+    def transform(s):
+        s["A"] = tq.tq_query_transform_split(s["q"], shared["perm"], shared["Pi_hi"], shared["Pi_lo"])
+
+    def score(s):
+        tq.tq_score_split(s["A"][0], s["A"][1], s["keys"], shared["cb_hi"], shared["cb_lo"], s["scores"])
+
+    for s in ring:                      # allocates each set's A once, before capture
+        transform(s)
+    A_fixed = [s["A"] for s in ring]
+
+    def transform_into(i):
+        A_hi, A_lo = A_fixed[i]
+        tq.tq_query_transform_split(ring[i]["q"], shared["perm"], shared["Pi_hi"], shared["Pi_lo"], A_hi, A_lo)
+
+    for i in range(args.warmup):
+        transform_into(i % nsets)
+        score(ring[i % nsets])
+    torch.cuda.synchronize()
+    steps = args.steps
+    chunks = [nsets] * (steps // nsets) + ([steps % nsets] if steps % nsets else [])
+    graphs = {}
+    for n in sorted(set(chunks)):
+        gt, gs = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gt):
+            for i in range(n):
+                transform_into(i)
+        with torch.cuda.graph(gs):
+            for i in range(n):
+                score(ring[i])
+        graphs[n] = (gt, gs)
+    for gt, gs in graphs.values():
+        gt.replay()
+        gs.replay()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in chunks]
+    t0 = time.perf_counter()
+    for n, ev in zip(chunks, evs):
+        gt, gs = graphs[n]
+        ev[0].record()
+        gt.replay()
+        ev[1].record()
+        gs.replay()
+        ev[2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    qt_us = 1e3 * sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    sc_us = 1e3 * sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    ms_per_step = elapsed * 1e3 / steps
+    tflops = flops / (sc_us * 1e-6) / 1e12
+    log(f"split: transform {qt_us:.2f} us, score {sc_us:.2f} us per launch, {tflops:.1f} TFLOP/s, "
+        f"{nbytes / (sc_us * 1e-6) / 1e9:.0f} GB/s algorithmic")
+    out = {
+        "metric": "query-key scores/sec, outlier-split keys (32 channels at 3 bits + the rest at 2)",
+        "value": w.pairs / (ms_per_step * 1e-3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded random packed codes and fp16 norms per instance, N(0,1) queries, Haar rotations",
+        "config": {"workload": w.name, "path": "split", "P": w.P, "H": w.H, "B": w.B, "S": w.S, "D": w.D,
+                   "D_hi": d_hi, "bits_hi": 3, "D_lo": d_lo, "bits_lo": 2},
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None, "kernel": "score_split_kernel",
+                     "flops_per_launch": flops, "bytes_per_launch": nbytes,
+                     "hbm_gbs": nbytes / (sc_us * 1e-6) / 1e9, "avg_launch_us": sc_us},
+        "tq_score_split_us": sc_us,
+        "tq_query_transform_split_us": qt_us,
+        "ring_sets": nsets,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import pack as opk
+        from oracle import split as osp
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        u_hi = opk.unpack_indices(ih[0], 3, d_hi)
+        u_lo = opk.unpack_indices(il[0], 2, d_lo)
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3:
+            t1 = time.perf_counter()
+            osp.scores_split_by_reconstruction(q[0], perm, d_hi, u_hi, nh[0].astype(np.float64), Pi_hi[0], cb_hi,
+                                               u_lo, nl[0].astype(np.float64), Pi_lo[0], cb_lo)
+            times.append(time.perf_counter() - t1)
+        med = sorted(times)[len(times) // 2]
+        out["cpu_baseline"] = {"value": w.B * w.S / med, "unit": "scores/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"problem 0 (B={w.B}, S={w.S}, D={w.D}) scored by float64 explicit "
+                                         f"reconstruction, median of {len(times)} runs ({sum(times):.1f} s total)"}
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -628,6 +763,9 @@ def main() -> int:
         return 0
     if args.path == "mse":
         print(json.dumps(bench_mse(args, w, device)), flush=True)
+        return 0
+    if args.path == "split":
+        print(json.dumps(bench_split(args, w, device)), flush=True)
         return 0
     kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, args.kernel)
     log(f"workload {w.describe()} kernel {kname}")

@@ -13,6 +13,8 @@ functions keep the C names:
     tq_attend_workspace_bytes(P, B, S, D)
     tq_query_transform_hadamard(q, signs)      -> A
     tq_score_mse(A, keys, codebook)            -> scores   (MSE-only keys: Values format)
+    tq_query_transform_split(q, perm, Pi_hi, Pi_lo, D_hi) -> (A_hi, A_lo)
+    tq_score_split(A_hi, A_lo, SplitKeys, codebook_hi, codebook_lo) -> scores
     tq_score_kernel_name(layout, bits, C, P, B, S, D, kernel)
 
 Only argument marshalling happens here: shapes, dtypes, contiguity and device
@@ -33,7 +35,7 @@ import torch
 
 __all__ = [
     "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform_hadamard",
-    "tq_score_mse", "tq_query_transform", "tq_score", "tq_score_with_kernel",
+    "tq_score_mse", "SplitKeys", "tq_query_transform_split", "tq_score_split", "tq_query_transform", "tq_score", "tq_score_with_kernel",
     "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
     "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
 ]
@@ -77,6 +79,10 @@ class _CValues(ctypes.Structure):
     ]
 
 
+class _CSplit(ctypes.Structure):
+    _fields_ = [("hi", _CValues), ("lo", _CValues)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
@@ -106,6 +112,10 @@ def _load():
     lib.tq_query_transform_hadamard.restype = i32
     lib.tq_score_mse.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, i32, i32, i32, i32, vp]
     lib.tq_score_mse.restype = i32
+    lib.tq_query_transform_split.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.tq_query_transform_split.restype = i32
+    lib.tq_score_split.argtypes = [vp, vp, ctypes.POINTER(_CSplit), vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    lib.tq_score_split.restype = i32
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     return lib
@@ -441,3 +451,62 @@ def tq_score_mse(A: torch.Tensor, keys: Values, codebook: torch.Tensor, scores: 
     _check(_lib.tq_score_mse(_ptr(A3), ctypes.byref(ck), _ptr(codebook), codebook.numel(), _ptr(scores),
                              P, B, S, D, _stream(A.device, stream)), "tq_score_mse")
     return scores.view(B, S) if squeeze else scores.view(P, B, S)
+
+
+@dataclass
+class SplitKeys:
+    """Outlier-split keys: one set of MSE-only codes per instance (hot channels, the rest)."""
+    hi: Values
+    lo: Values
+
+
+def tq_query_transform_split(q: torch.Tensor, perm: torch.Tensor, Pi_hi: torch.Tensor, Pi_lo: torch.Tensor,
+                             A_hi: torch.Tensor | None = None, A_lo: torch.Tensor | None = None, stream=None):
+    """(A_hi, A_lo) = (Pi_hi q[perm[:D_hi]], Pi_lo q[perm[D_hi:]]). q [P,B,D]; perm int32 [D];
+    Pi_hi [H,D_hi,D_hi]; Pi_lo [H,D-D_hi,D-D_hi]."""
+    q3 = _as3(_gpu(q, "q", torch.float32))
+    _gpu(perm, "perm", torch.int32)
+    Ph = _as3(_gpu(Pi_hi, "Pi_hi", torch.float32))
+    Pl = _as3(_gpu(Pi_lo, "Pi_lo", torch.float32))
+    P, B, D = q3.shape
+    H, D_hi = Ph.shape[0], Ph.shape[-1]
+    if perm.numel() != D or Ph.shape != (H, D_hi, D_hi) or Pl.shape != (H, D - D_hi, D - D_hi):
+        raise ValueError("perm must be [D], Pi_hi [H,D_hi,D_hi], Pi_lo [H,D-D_hi,D-D_hi]")
+    if A_hi is None:
+        A_hi = torch.empty((P, B, D_hi), dtype=torch.float32, device=q.device)
+    if A_lo is None:
+        A_lo = torch.empty((P, B, D - D_hi), dtype=torch.float32, device=q.device)
+    _gpu(A_hi, "A_hi", torch.float32)
+    _gpu(A_lo, "A_lo", torch.float32)
+    if A_hi.numel() != P * B * D_hi or A_lo.numel() != P * B * (D - D_hi):
+        raise ValueError("A_hi must hold P*B*D_hi floats and A_lo P*B*(D-D_hi)")
+    _check(_lib.tq_query_transform_split(_ptr(q3), _ptr(perm), _ptr(Ph), _ptr(Pl), _ptr(A_hi), _ptr(A_lo),
+                                         P, H, B, D, D_hi, _stream(q.device, stream)), "tq_query_transform_split")
+    return A_hi, A_lo
+
+
+def tq_score_split(A_hi: torch.Tensor, A_lo: torch.Tensor, keys: SplitKeys, codebook_hi: torch.Tensor,
+                   codebook_lo: torch.Tensor, scores: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Scores [P,B,S]: the two instances' MSE scores added."""
+    Ah = _as3(_gpu(A_hi, "A_hi", torch.float32))
+    Al = _as3(_gpu(A_lo, "A_lo", torch.float32))
+    _gpu(codebook_hi, "codebook_hi", torch.float32)
+    _gpu(codebook_lo, "codebook_lo", torch.float32)
+    P, B, D_hi = Ah.shape
+    D_lo = Al.shape[-1]
+    if Al.shape[:2] != (P, B):
+        raise ValueError("A_hi and A_lo must share [P, B]")
+    ch, Ph, S = keys.hi._c(D_hi)
+    cl, Pl, Sl = keys.lo._c(D_lo)
+    if (Ph, Pl, Sl) != (P, P, S):
+        raise ValueError("both instances must hold [P, S] keys matching A")
+    if scores is None:
+        scores = torch.empty((P, B, S), dtype=torch.float32, device=A_hi.device)
+    _gpu(scores, "scores", torch.float32)
+    if scores.numel() != P * B * S:
+        raise ValueError("scores must hold P*B*S floats")
+    c = _CSplit(ch, cl)
+    _check(_lib.tq_score_split(_ptr(Ah), _ptr(Al), ctypes.byref(c), _ptr(codebook_hi), codebook_hi.numel(),
+                               _ptr(codebook_lo), codebook_lo.numel(), _ptr(scores), P, B, S, D_hi, D_lo,
+                               _stream(A_hi.device, stream)), "tq_score_split")
+    return scores.view(P, B, S)

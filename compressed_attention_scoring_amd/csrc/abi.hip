@@ -233,6 +233,62 @@ int tq_score_mse(const float* A, const tq_mse_codes* keys, const float* codebook
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
+int tq_query_transform_split(const float* q, const int32_t* perm, const float* Pi_hi, const float* Pi_lo, float* A_hi,
+                             float* A_lo, int P, int H, int B, int D, int D_hi, void* stream) {
+    if (P < 0 || H <= 0 || B < 0 || D <= 0 || P % H != 0 || D_hi <= 0 || D_hi >= D) return TQ_ERR_ARG;
+    if (D > TQ_MAX_D) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!q || !perm || !Pi_hi || !Pi_lo || !A_hi || !A_lo) return TQ_ERR_ARG;
+    if (P > 65535 || !fits(P, B, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(perm) || !aligned16(Pi_hi) || !aligned16(Pi_lo) || !aligned16(A_hi) ||
+        !aligned16(A_lo))
+        return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_query_transform_split(q, perm, Pi_hi, Pi_lo, A_hi, A_lo, P, H, B, D, D_hi,
+                                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+namespace {
+// Format of one MSE instance for the split scorer: 0 unpacked, else the packed width.
+int split_bits(const tq_mse_codes& c, int C, int D, int* bits) {
+    if (c.layout != TQ_UNPACKED && c.layout != TQ_PACKED) return TQ_ERR_ARG;
+    if (D < 8 || D > TQ_MAX_D || D % 8 != 0) return TQ_ERR_UNSUPPORTED;
+    if (c.layout == TQ_UNPACKED) {
+        if (C < 1 || C > 256) return TQ_ERR_UNSUPPORTED;
+        *bits = 0;
+    } else {
+        if ((c.bits != 2 && c.bits != 3) || C != (1 << c.bits)) return TQ_ERR_UNSUPPORTED;
+        *bits = c.bits;
+    }
+    return TQ_OK;
+}
+}  // namespace
+
+int tq_score_split(const float* A_hi, const float* A_lo, const tq_split_codes* keys, const float* codebook_hi, int C_hi,
+                   const float* codebook_lo, int C_lo, float* scores, int P, int B, int S, int D_hi, int D_lo,
+                   void* stream) {
+    if (!keys || P < 0 || B < 0 || S < 0 || D_hi <= 0 || D_lo <= 0) return TQ_ERR_ARG;
+    int bh = 0, bl = 0;
+    int kc = split_bits(keys->hi, C_hi, D_hi, &bh);
+    if (kc != TQ_OK) return kc;
+    kc = split_bits(keys->lo, C_lo, D_lo, &bl);
+    if (kc != TQ_OK) return kc;
+    if (P == 0 || B == 0 || S == 0) return TQ_OK;   // empty call: nothing to launch
+    if (!A_hi || !A_lo || !codebook_hi || !codebook_lo || !scores || !keys->hi.idx || !keys->hi.norm ||
+        !keys->lo.idx || !keys->lo.norm)
+        return TQ_ERR_ARG;
+    if (P > 65535 || B > 262144 || !fits(P, B, S) || !fits(P, S, D_hi + D_lo)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(A_hi) || !aligned16(A_lo) || !aligned16(codebook_hi) || !aligned16(codebook_lo) ||
+        !aligned16(scores) || !aligned16(keys->hi.idx) || !aligned16(keys->hi.norm) || !aligned16(keys->lo.idx) ||
+        !aligned16(keys->lo.norm))
+        return TQ_ERR_ALIGN;
+    const tq::SplitStreams k{static_cast<const uint8_t*>(keys->hi.idx), keys->hi.norm,
+                             static_cast<const uint8_t*>(keys->lo.idx), keys->lo.norm};
+    const hipError_t e = tq::launch_score_split(A_hi, A_lo, k, bh, bl, codebook_hi, C_hi, codebook_lo, C_lo, scores,
+                                                P, B, S, D_hi, D_lo, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                     int P, int S, int D, void* stream) {
     if (P < 0 || S < 0) return TQ_ERR_ARG;

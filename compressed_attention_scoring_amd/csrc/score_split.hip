@@ -1,0 +1,188 @@
+// The outlier split ("TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits",
+// section 7): two MSE-only quantizer instances per head over disjoint channel
+// sets, the hot channels with more bits, each with its own rotation and norm.
+// A key's score is the sum of its instances' scores:
+//   scores[p,b,s] = norm_hi[s] sum_i A_hi[b,i] cb_hi[idx_hi[s,i]]
+//                 + norm_lo[s] sum_j A_lo[b,j] cb_lo[idx_lo[s,j]],
+// with A_hi = Pi_hi q[hot channels] and A_lo = Pi_lo q[other channels].
+//
+// split_query_kernel: one workgroup per query; the query's channels, permuted
+// so the hot ones come first, are staged in LDS and each output coordinate is
+// one thread's dot product with its row of the instance's rotation (the
+// instances are small and not powers of two, so a dense product).
+//
+// score_split_kernel: one key per lane and QB queries per pass, both instances
+// in the same pass so each score is written once. The query operands of both
+// instances sit in LDS laid out [coordinate][query] (one broadcast read serves
+// the wavefront), as do both codebooks; fp32 FMAs. Index rows are decoded
+// eight coordinates at a time from either layout (bytes, or LSB-first 2- or
+// 3-bit streams).
+#include "tq_common.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void split_query_kernel(const float* __restrict__ q,
+                                                               const int32_t* __restrict__ perm,
+                                                               const float* __restrict__ Pi_hi,
+                                                               const float* __restrict__ Pi_lo,
+                                                               float* __restrict__ A_hi, float* __restrict__ A_lo,
+                                                               int H, int B, int D, int D_hi) {
+    extern __shared__ float qs[];                 // [D] permuted query
+    const int b = blockIdx.x;
+    const int p = blockIdx.y;
+    const int h = p % H;
+    const float* src = q + ((int64_t)p * B + b) * D;
+    for (int i = threadIdx.x; i < D; i += kThreads) qs[i] = src[perm[i]];
+    __syncthreads();
+    const int D_lo = D - D_hi;
+    for (int i = threadIdx.x; i < D; i += kThreads) {
+        const bool hi = i < D_hi;
+        const int n = hi ? D_hi : D_lo;           // size of this coordinate's instance
+        const int r = hi ? i : i - D_hi;          // its row in the instance's rotation
+        const float* row = (hi ? Pi_hi + (int64_t)h * D_hi * D_hi : Pi_lo + (int64_t)h * D_lo * D_lo) + (int64_t)r * n;
+        const float* x = qs + (hi ? 0 : D_hi);
+        float acc = 0.f;
+        for (int j = 0; j < n; ++j) acc = fmaf(row[j], x[j], acc);
+        if (hi) A_hi[((int64_t)p * B + b) * D_hi + r] = acc;
+        else A_lo[((int64_t)p * B + b) * D_lo + r] = acc;
+    }
+}
+
+// Eight consecutive coordinates (chunk j) of a key's index row in layout BITS
+// (0: one byte per index).
+template <int BITS>
+__device__ __forceinline__ void indices8(const uint8_t* __restrict__ row, int j, int (&code)[8]) {
+    if constexpr (BITS == 0) {
+        const uint64_t v = *reinterpret_cast<const uint64_t*>(row + 8 * j);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) code[t] = (int)((v >> (8 * t)) & 0xffu);
+    } else {
+        const uint8_t* b = row + BITS * j;        // 8 indices take BITS bytes
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) w |= (uint32_t)b[k] << (8 * k);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) code[t] = (int)((w >> (BITS * t)) & ((1u << BITS) - 1u));
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ float norm_of(const void* __restrict__ norm, int64_t key) {
+    if constexpr (BITS == 0) return reinterpret_cast<const float*>(norm)[key];
+    else return (float)reinterpret_cast<const _Float16*>(norm)[key];
+}
+
+// Accumulate one instance's dot products for QB queries.
+template <int BITS, int QB>
+__device__ __forceinline__ void instance_dots(const uint8_t* __restrict__ row, int n, const float* __restrict__ At,
+                                              const float* __restrict__ cb, float (&m)[QB]) {
+    for (int j = 0; j < n / 8; ++j) {
+        int code[8];
+        indices8<BITS>(row, j, code);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int d = 8 * j + t;
+            const float c = cb[code[t]];
+#pragma unroll
+            for (int i = 0; i < QB; ++i) m[i] = fmaf(At[d * QB + i], c, m[i]);
+        }
+    }
+}
+
+template <int BH, int BL, int QB>
+__global__ __launch_bounds__(kThreads) void score_split_kernel(
+    const float* __restrict__ A_hi, const float* __restrict__ A_lo, const uint8_t* __restrict__ idx_hi,
+    const void* __restrict__ norm_hi, const uint8_t* __restrict__ idx_lo, const void* __restrict__ norm_lo,
+    const float* __restrict__ cb_hi, int C_hi, const float* __restrict__ cb_lo, int C_lo,
+    float* __restrict__ scores, int B, int S, int D_hi, int D_lo) {
+    extern __shared__ float lds[];
+    float* Ah = lds;                       // [D_hi][QB]
+    float* Al = Ah + D_hi * QB;            // [D_lo][QB]
+    float* ch = Al + D_lo * QB;            // [C_hi]
+    float* cl = ch + C_hi;                 // [C_lo]
+    const int p = blockIdx.z;
+    const int b0 = blockIdx.y * QB;
+    for (int e = threadIdx.x; e < QB * D_hi; e += kThreads) {
+        const int i = e / D_hi, d = e % D_hi;
+        Ah[d * QB + i] = b0 + i < B ? A_hi[((int64_t)p * B + b0 + i) * D_hi + d] : 0.f;
+    }
+    for (int e = threadIdx.x; e < QB * D_lo; e += kThreads) {
+        const int i = e / D_lo, d = e % D_lo;
+        Al[d * QB + i] = b0 + i < B ? A_lo[((int64_t)p * B + b0 + i) * D_lo + d] : 0.f;
+    }
+    for (int e = threadIdx.x; e < C_hi; e += kThreads) ch[e] = cb_hi[e];
+    for (int e = threadIdx.x; e < C_lo; e += kThreads) cl[e] = cb_lo[e];
+    __syncthreads();
+
+    const int s = blockIdx.x * kThreads + threadIdx.x;
+    if (s >= S) return;
+    const int64_t key = (int64_t)p * S + s;
+    const int64_t row_hi = BH == 0 ? D_hi : (int64_t)D_hi * BH / 8;
+    const int64_t row_lo = BL == 0 ? D_lo : (int64_t)D_lo * BL / 8;
+    float mh[QB], ml[QB];
+#pragma unroll
+    for (int i = 0; i < QB; ++i) mh[i] = ml[i] = 0.f;
+    instance_dots<BH, QB>(idx_hi + key * row_hi, D_hi, Ah, ch, mh);
+    instance_dots<BL, QB>(idx_lo + key * row_lo, D_lo, Al, cl, ml);
+    const float nh = norm_of<BH>(norm_hi, key);
+    const float nl = norm_of<BL>(norm_lo, key);
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+        if (b0 + i < B) scores[((int64_t)p * B + b0 + i) * S + s] = fmaf(nh, mh[i], nl * ml[i]);
+    }
+}
+
+template <int BH, int BL, int QB>
+hipError_t launch_split_qb(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
+                           const float* cb_lo, int C_lo, float* scores, int P, int B, int S, int D_hi, int D_lo,
+                           hipStream_t stream) {
+    const dim3 grid((S + kThreads - 1) / kThreads, (B + QB - 1) / QB, P);
+    const size_t lds = (size_t)((D_hi + D_lo) * QB + C_hi + C_lo) * sizeof(float);
+    hipLaunchKernelGGL((score_split_kernel<BH, BL, QB>), grid, dim3(kThreads), lds, stream, A_hi, A_lo, k.idx_hi,
+                       k.norm_hi, k.idx_lo, k.norm_lo, cb_hi, C_hi, cb_lo, C_lo, scores, B, S, D_hi, D_lo);
+    return hipGetLastError();
+}
+
+template <int BH, int BL>
+hipError_t launch_split_bits(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
+                             const float* cb_lo, int C_lo, float* scores, int P, int B, int S, int D_hi, int D_lo,
+                             hipStream_t stream) {
+    // queries per lane: LDS holds (D_hi + D_lo) * QB floats
+    if (B <= 1) return launch_split_qb<BH, BL, 1>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    if (B <= 2) return launch_split_qb<BH, BL, 2>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    if (B <= 4 || D_hi + D_lo > 512)
+        return launch_split_qb<BH, BL, 4>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    return launch_split_qb<BH, BL, 8>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+}
+
+template <int BH>
+hipError_t launch_split_lo(int bits_lo, const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi,
+                           int C_hi, const float* cb_lo, int C_lo, float* scores, int P, int B, int S, int D_hi,
+                           int D_lo, hipStream_t stream) {
+    if (bits_lo == 0) return launch_split_bits<BH, 0>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    if (bits_lo == 2) return launch_split_bits<BH, 2>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    return launch_split_bits<BH, 3>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+}
+
+}  // namespace
+
+hipError_t launch_query_transform_split(const float* q, const int32_t* perm, const float* Pi_hi, const float* Pi_lo,
+                                        float* A_hi, float* A_lo, int P, int H, int B, int D, int D_hi,
+                                        hipStream_t stream) {
+    hipLaunchKernelGGL(split_query_kernel, dim3((unsigned)B, (unsigned)P), dim3(kThreads), (size_t)D * sizeof(float),
+                       stream, q, perm, Pi_hi, Pi_lo, A_hi, A_lo, H, B, D, D_hi);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_split(const float* A_hi, const float* A_lo, SplitStreams k, int bits_hi, int bits_lo,
+                              const float* cb_hi, int C_hi, const float* cb_lo, int C_lo, float* scores, int P,
+                              int B, int S, int D_hi, int D_lo, hipStream_t stream) {
+    if (bits_hi == 0) return launch_split_lo<0>(bits_lo, A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    if (bits_hi == 2) return launch_split_lo<2>(bits_lo, A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    return launch_split_lo<3>(bits_lo, A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+}
+
+}  // namespace tq

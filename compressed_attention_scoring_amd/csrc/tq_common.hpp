@@ -86,6 +86,21 @@ bool hadamard_supported(int D);
 hipError_t launch_query_transform_hadamard(const float* q, const float* signs, float* A, int P, int H, int B,
                                            int D, hipStream_t stream);
 
+// The outlier split: two MSE-only instances per head (hot channels, the rest).
+struct SplitStreams {
+    const uint8_t* idx_hi;
+    const void* norm_hi;
+    const uint8_t* idx_lo;
+    const void* norm_lo;
+};
+hipError_t launch_query_transform_split(const float* q, const int32_t* perm, const float* Pi_hi, const float* Pi_lo,
+                                        float* A_hi, float* A_lo, int P, int H, int B, int D, int D_hi,
+                                        hipStream_t stream);
+// bits_hi, bits_lo: 0 for one byte per index, else 2 or 3 (packed)
+hipError_t launch_score_split(const float* A_hi, const float* A_lo, SplitStreams k, int bits_hi, int bits_lo,
+                              const float* cb_hi, int C_hi, const float* cb_lo, int C_lo, float* scores, int P,
+                              int B, int S, int D_hi, int D_lo, hipStream_t stream);
+
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                          int P, int S, int D, hipStream_t stream);

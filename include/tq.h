@@ -314,6 +314,51 @@ int tq_query_transform_hadamard(const float* q, const float* signs, float* A,
 int tq_score_mse(const float* A, const tq_mse_codes* keys, const float* codebook, int C,
                  float* scores, int P, int B, int S, int D, void* stream);
 
+/*
+ * The outlier split ("TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits",
+ * section 7): two MSE-only instances per head over disjoint channel sets, the
+ * hot channels with more bits, each with its own rotation and its own norm.
+ * A key stores one tq_mse_codes per instance, over D_hi and D_lo coordinates.
+ */
+typedef struct tq_split_codes {
+    tq_mse_codes hi;   /* the hot channels' instance */
+    tq_mse_codes lo;   /* the other channels' instance */
+} tq_split_codes;
+
+/*
+ * tq_query_transform_split: A_hi = Pi_hi q[perm[0 .. D_hi)] and
+ * A_lo = Pi_lo q[perm[D_hi .. D)] for every query (dense fp32 products).
+ *
+ *   q      float32 [P, B, D]
+ *   perm   int32 [D]             a permutation of 0..D-1: the hot channels, then
+ *                                the others (not checked)
+ *   Pi_hi  float32 [H, D_hi, D_hi], Pi_lo float32 [H, D - D_hi, D - D_hi]
+ *   A_hi   float32 [P, B, D_hi],  A_lo float32 [P, B, D - D_hi]   outputs
+ *
+ * 0 < D_hi < D <= TQ_MAX_D.
+ */
+int tq_query_transform_split(const float* q, const int32_t* perm, const float* Pi_hi, const float* Pi_lo,
+                             float* A_hi, float* A_lo, int P, int H, int B, int D, int D_hi, void* stream);
+
+/*
+ * tq_score_split: raw scores against outlier-split keys, the sum of the two
+ * instances' MSE scores:
+ *
+ *   scores[p,b,s] = norm_hi[p,s] * sum_i A_hi[p,b,i] * codebook_hi[idx_hi[p,s,i]]
+ *                 + norm_lo[p,s] * sum_j A_lo[p,b,j] * codebook_lo[idx_lo[p,s,j]]
+ *
+ *   keys       host pointer to the two instances' codes (layouts as tq_mse_codes;
+ *              each instance has its own layout and width)
+ *   codebooks  float32 [C_hi], [C_lo]: unpacked C <= 256, packed C == 2^bits
+ *   scores     float32 [P, B, S]   output
+ *
+ * D_hi and D_lo multiples of 8 in [8, TQ_MAX_D]. fp32 arithmetic (vector ALU):
+ * within 1e-4 * (1 + |exact|) of the exact value.
+ */
+int tq_score_split(const float* A_hi, const float* A_lo, const tq_split_codes* keys,
+                   const float* codebook_hi, int C_hi, const float* codebook_lo, int C_lo,
+                   float* scores, int P, int B, int S, int D_hi, int D_lo, void* stream);
+
 /* tq_status_string: static description of a status code. */
 const char* tq_status_string(int status);
 

@@ -12,7 +12,7 @@ import compressed_attention_scoring_amd as tq
 EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
-    "tq_query_transform_hadamard", "tq_score_mse",
+    "tq_query_transform_hadamard", "tq_score_mse", "tq_query_transform_split", "tq_score_split",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -212,3 +212,27 @@ def test_score_mse_rejects_bad_arguments():
     assert f(16, keys(), 16, 4, 16, 1, 4, 1 << 24, 128, None) == UNSUP
     assert f(16, keys(idx=20), 16, 4, 16, 1, 4, 8, 128, None) == ALIGN
     assert f(None, keys(idx=None, norm=None), None, 4, None, 1, 4, 0, 128, None) == OK
+
+
+def test_split_rejects_bad_arguments():
+    qf = tq._lib.tq_query_transform_split
+    assert qf(16, 16, 16, 16, 16, 16, 1, 1, 2, 128, 0, None) == ARG          # D_hi = 0
+    assert qf(16, 16, 16, 16, 16, 16, 1, 1, 2, 128, 128, None) == ARG        # D_hi = D
+    assert qf(16, 16, 16, 16, 16, 16, 3, 2, 2, 128, 32, None) == ARG         # P % H
+    assert qf(16, None, 16, 16, 16, 16, 1, 1, 2, 128, 32, None) == ARG
+    assert qf(16, 16, 16, 16, 16, 16, 1, 1, 2, 2048, 32, None) == UNSUP
+    assert qf(16, 20, 16, 16, 16, 16, 1, 1, 2, 128, 32, None) == ALIGN
+    assert qf(None, None, None, None, None, None, 1, 1, 0, 128, 32, None) == OK
+    sf = tq._lib.tq_score_split
+    inst = lambda layout=1, bits=3, idx=16, norm=16: tq._CValues(layout, bits, idx, norm)
+    keys = lambda hi=None, lo=None: ctypes.byref(tq._CSplit(hi or inst(), lo or inst(bits=2)))
+    assert sf(16, 16, None, 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ARG
+    assert sf(16, 16, keys(), 16, 8, 16, 4, 16, 1, 4, 8, 0, 96, None) == ARG
+    assert sf(16, 16, keys(hi=inst(layout=7)), 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ARG
+    assert sf(16, 16, keys(), 16, 4, 16, 4, 16, 1, 4, 8, 32, 96, None) == UNSUP     # C_hi != 2^3
+    assert sf(16, 16, keys(), 16, 8, 16, 4, 16, 1, 4, 8, 36, 92, None) == UNSUP     # not multiples of 8
+    assert sf(16, 16, keys(hi=inst(layout=0, bits=0)), 16, 300, 16, 4, 16, 1, 4, 8, 32, 96, None) == UNSUP
+    assert sf(None, 16, keys(), 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ARG
+    assert sf(16, 16, keys(lo=inst(bits=2, norm=None)), 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ARG
+    assert sf(16, 24, keys(), 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ALIGN
+    assert sf(None, None, keys(), None, 8, None, 4, None, 1, 4, 0, 32, 96, None) == OK
