@@ -12,9 +12,9 @@
 // instances are small and not powers of two, so a dense product).
 //
 // score_split_kernel: one key per lane and QB queries per pass, both instances
-// in the same pass so each score is written once. The query operands of both
-// instances sit in LDS laid out [coordinate][query] (one broadcast read serves
-// the wavefront), as do both codebooks; fp32 FMAs. Index rows are decoded
+// in the same pass so each score is written once. The query operands are the
+// same for every lane, so they are read with scalar loads and enter the FMAs
+// from scalar registers; the codebooks sit in LDS; fp32 FMAs. Index rows are decoded
 // eight coordinates at a time from either layout (bytes, or LSB-first 2- or
 // 3-bit streams).
 #include "tq_common.hpp"
@@ -75,19 +75,25 @@ __device__ __forceinline__ float norm_of(const void* __restrict__ norm, int64_t 
     else return (float)reinterpret_cast<const _Float16*>(norm)[key];
 }
 
-// Accumulate one instance's dot products for QB queries.
+// Accumulate one instance's dot products for QB queries. `A` points at row b0
+// of the instance's query operands and `rows` clamps the row index; every
+// address into A is the same for the whole wavefront, so those loads are scalar
+// and the FMAs take their query operand from scalar registers.
 template <int BITS, int QB>
-__device__ __forceinline__ void instance_dots(const uint8_t* __restrict__ row, int n, const float* __restrict__ At,
+__device__ __forceinline__ void instance_dots(const uint8_t* __restrict__ row, int n,
+                                              const float* __restrict__ A, int rows,
                                               const float* __restrict__ cb, float (&m)[QB]) {
     for (int j = 0; j < n / 8; ++j) {
         int code[8];
         indices8<BITS>(row, j, code);
+        float c[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int d = 8 * j + t;
-            const float c = cb[code[t]];
+        for (int t = 0; t < 8; ++t) c[t] = cb[code[t]];
 #pragma unroll
-            for (int i = 0; i < QB; ++i) m[i] = fmaf(At[d * QB + i], c, m[i]);
+        for (int i = 0; i < QB; ++i) {
+            const float* a = A + (int64_t)min(i, rows - 1) * n + 8 * j;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m[i] = fmaf(a[t], c[t], m[i]);
         }
     }
 }
@@ -98,21 +104,11 @@ __global__ __launch_bounds__(kThreads) void score_split_kernel(
     const void* __restrict__ norm_hi, const uint8_t* __restrict__ idx_lo, const void* __restrict__ norm_lo,
     const float* __restrict__ cb_hi, int C_hi, const float* __restrict__ cb_lo, int C_lo,
     float* __restrict__ scores, int B, int S, int D_hi, int D_lo) {
-    extern __shared__ float lds[];
-    float* Ah = lds;                       // [D_hi][QB]
-    float* Al = Ah + D_hi * QB;            // [D_lo][QB]
-    float* ch = Al + D_lo * QB;            // [C_hi]
-    float* cl = ch + C_hi;                 // [C_lo]
+    __shared__ float ch[256];
+    __shared__ float cl[256];
     const int p = blockIdx.z;
     const int b0 = blockIdx.y * QB;
-    for (int e = threadIdx.x; e < QB * D_hi; e += kThreads) {
-        const int i = e / D_hi, d = e % D_hi;
-        Ah[d * QB + i] = b0 + i < B ? A_hi[((int64_t)p * B + b0 + i) * D_hi + d] : 0.f;
-    }
-    for (int e = threadIdx.x; e < QB * D_lo; e += kThreads) {
-        const int i = e / D_lo, d = e % D_lo;
-        Al[d * QB + i] = b0 + i < B ? A_lo[((int64_t)p * B + b0 + i) * D_lo + d] : 0.f;
-    }
+    const int rows = min(QB, B - b0);            // valid queries of this group
     for (int e = threadIdx.x; e < C_hi; e += kThreads) ch[e] = cb_hi[e];
     for (int e = threadIdx.x; e < C_lo; e += kThreads) cl[e] = cb_lo[e];
     __syncthreads();
@@ -125,13 +121,13 @@ __global__ __launch_bounds__(kThreads) void score_split_kernel(
     float mh[QB], ml[QB];
 #pragma unroll
     for (int i = 0; i < QB; ++i) mh[i] = ml[i] = 0.f;
-    instance_dots<BH, QB>(idx_hi + key * row_hi, D_hi, Ah, ch, mh);
-    instance_dots<BL, QB>(idx_lo + key * row_lo, D_lo, Al, cl, ml);
+    instance_dots<BH, QB>(idx_hi + key * row_hi, D_hi, A_hi + ((int64_t)p * B + b0) * D_hi, rows, ch, mh);
+    instance_dots<BL, QB>(idx_lo + key * row_lo, D_lo, A_lo + ((int64_t)p * B + b0) * D_lo, rows, cl, ml);
     const float nh = norm_of<BH>(norm_hi, key);
     const float nl = norm_of<BL>(norm_lo, key);
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
-        if (b0 + i < B) scores[((int64_t)p * B + b0 + i) * S + s] = fmaf(nh, mh[i], nl * ml[i]);
+        if (i < rows) scores[((int64_t)p * B + b0 + i) * S + s] = fmaf(nh, mh[i], nl * ml[i]);
     }
 }
 
@@ -140,8 +136,7 @@ hipError_t launch_split_qb(const float* A_hi, const float* A_lo, SplitStreams k,
                            const float* cb_lo, int C_lo, float* scores, int P, int B, int S, int D_hi, int D_lo,
                            hipStream_t stream) {
     const dim3 grid((S + kThreads - 1) / kThreads, (B + QB - 1) / QB, P);
-    const size_t lds = (size_t)((D_hi + D_lo) * QB + C_hi + C_lo) * sizeof(float);
-    hipLaunchKernelGGL((score_split_kernel<BH, BL, QB>), grid, dim3(kThreads), lds, stream, A_hi, A_lo, k.idx_hi,
+    hipLaunchKernelGGL((score_split_kernel<BH, BL, QB>), grid, dim3(kThreads), 0, stream, A_hi, A_lo, k.idx_hi,
                        k.norm_hi, k.idx_lo, k.norm_lo, cb_hi, C_hi, cb_lo, C_lo, scores, B, S, D_hi, D_lo);
     return hipGetLastError();
 }
@@ -150,12 +145,19 @@ template <int BH, int BL>
 hipError_t launch_split_bits(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
                              const float* cb_lo, int C_lo, float* scores, int P, int B, int S, int D_hi, int D_lo,
                              hipStream_t stream) {
-    // queries per lane: LDS holds (D_hi + D_lo) * QB floats
+    // Queries per lane: a codebook lookup serves QB FMAs, but fewer, longer query
+    // groups mean fewer wavefronts. Take the largest QB that still gives about
+    // 1024 workgroups (four wavefronts per SIMD); measured at B = 32, S = 32 768:
+    // 10.6 us with QB = 4 against 20.2 us with QB = 16, while B = 128, S = 262 144
+    // prefers 16 (144 us against 167).
+    const int64_t kb = ((int64_t)S + kThreads - 1) / kThreads * P;
     if (B <= 1) return launch_split_qb<BH, BL, 1>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
     if (B <= 2) return launch_split_qb<BH, BL, 2>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
-    if (B <= 4 || D_hi + D_lo > 512)
-        return launch_split_qb<BH, BL, 4>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
-    return launch_split_qb<BH, BL, 8>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    if (B > 8 && kb * ((B + 15) / 16) >= 1024)
+        return launch_split_qb<BH, BL, 16>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    if (B > 4 && kb * ((B + 7) / 8) >= 1024)
+        return launch_split_qb<BH, BL, 8>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
+    return launch_split_qb<BH, BL, 4>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
 }
 
 template <int BH>
