@@ -11,6 +11,7 @@ functions keep the C names:
     tq_compress_keys(keys, Pi, S_mat, codebook, layout, bits) -> Keys
     tq_attend(scores, values, codebook, Pi_v, scale) -> out
     tq_attend_workspace_bytes(P, B, S, D)
+    tq_score_attend(A, T, keys, codebook, values, codebook_v, Pi_v, scale) -> out   (fused decode step)
     tq_query_transform_hadamard(q, signs)      -> A
     tq_score_mse(A, keys, codebook)            -> scores   (MSE-only keys: Values format)
     tq_query_transform_split(q, perm, Pi_hi, Pi_lo, D_hi) -> (A_hi, A_lo)
@@ -35,7 +36,7 @@ import torch
 
 __all__ = [
     "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform_hadamard",
-    "tq_score_mse", "SplitKeys", "tq_query_transform_split", "tq_score_split", "tq_query_transform", "tq_score", "tq_score_with_kernel",
+    "tq_score_mse", "tq_score_attend", "tq_score_attend_workspace_bytes", "SplitKeys", "tq_query_transform_split", "tq_score_split", "tq_query_transform", "tq_score", "tq_score_with_kernel",
     "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
     "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
 ]
@@ -108,6 +109,11 @@ def _load():
     lib.tq_attend.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp, vp, ctypes.c_size_t,
                               i32, i32, i32, i32, i32, vp]
     lib.tq_attend.restype = i32
+    lib.tq_score_attend_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.tq_score_attend_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq_score_attend.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, ctypes.POINTER(_CValues), vp, i32, vp,
+                                    ctypes.c_float, vp, vp, ctypes.c_size_t, i32, i32, i32, i32, i32, vp]
+    lib.tq_score_attend.restype = i32
     lib.tq_query_transform_hadamard.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     lib.tq_query_transform_hadamard.restype = i32
     lib.tq_score_mse.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, i32, i32, i32, i32, vp]
@@ -510,3 +516,46 @@ def tq_score_split(A_hi: torch.Tensor, A_lo: torch.Tensor, keys: SplitKeys, code
                                _ptr(codebook_lo), codebook_lo.numel(), _ptr(scores), P, B, S, D_hi, D_lo,
                                _stream(A_hi.device, stream)), "tq_score_split")
     return scores.view(P, B, S)
+
+
+def tq_score_attend_workspace_bytes(P: int, B: int, S: int, D: int) -> int:
+    """Workspace bytes tq_score_attend needs for this shape."""
+    return int(_lib.tq_score_attend_workspace_bytes(int(P), int(B), int(S), int(D)))
+
+
+def tq_score_attend(A: torch.Tensor, T: torch.Tensor, keys: Keys, codebook: torch.Tensor, values: Values,
+                    codebook_v: torch.Tensor, Pi_v: torch.Tensor, scale: float | None = None,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """The fused decode step: softmax(scale * scores) times the dequantized values,
+    without writing the scores. out [P,B,D]."""
+    A3 = _as3(_gpu(A, "A", torch.float32))
+    T3 = _as3(_gpu(T, "T", torch.float32))
+    _gpu(codebook, "codebook", torch.float32)
+    _gpu(codebook_v, "codebook_v", torch.float32)
+    Pv = _as3(_gpu(Pi_v, "Pi_v", torch.float32))
+    P, B, D = A3.shape
+    H = Pv.shape[0]
+    if T3.shape != A3.shape or Pv.shape != (H, D, D):
+        raise ValueError("T must match A and Pi_v must be [H, D, D]")
+    ck, Pk, S = keys._c(D)
+    cv, Pv_, Sv = values._c(D)
+    if (Pk, Pv_, Sv) != (P, P, S):
+        raise ValueError("keys and values must hold [P, S] vectors matching A")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dev = A.device
+    if out is None:
+        out = torch.empty((P, B, D), dtype=torch.float32, device=dev)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != P * B * D:
+        raise ValueError("out must hold P*B*D floats")
+    need = tq_score_attend_workspace_bytes(P, B, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _gpu(workspace, "workspace", torch.uint8)
+    _check(_lib.tq_score_attend(_ptr(A3), _ptr(T3), ctypes.byref(ck), _ptr(codebook), codebook.numel(),
+                                ctypes.byref(cv), _ptr(codebook_v), codebook_v.numel(), _ptr(Pv), float(scale),
+                                _ptr(out), _ptr(workspace), workspace.numel(), P, H, B, S, D, _stream(dev, stream)),
+           "tq_score_attend")
+    return out.view(P, B, D)

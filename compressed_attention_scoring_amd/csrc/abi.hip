@@ -204,6 +204,48 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
+size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D) {
+    if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
+    int chunk = 0, nch = 0;
+    tq::score_attend_plan(P, B, S, chunk, nch);
+    return (size_t)((int64_t)P * B * nch * (D + 2) * (int64_t)sizeof(float));
+}
+
+int tq_score_attend(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
+                    const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v, float scale,
+                    float* out, void* workspace, size_t workspace_bytes, int P, int H, int B, int S, int D,
+                    void* stream) {
+    if (!values || P < 0 || B < 0 || S < 0 || H <= 0 || P % H != 0) return TQ_ERR_ARG;
+    int kc = check_format(keys, C, D, true);
+    if (kc != TQ_OK) return kc;
+    if (values->layout != TQ_UNPACKED && values->layout != TQ_PACKED) return TQ_ERR_ARG;
+    const int bits = keys->layout == TQ_PACKED ? keys->bits : 0;
+    const int vbits = values->layout == TQ_PACKED ? values->bits : 0;
+    if (values->layout == TQ_PACKED && ((vbits != 2 && vbits != 3) || C_v != (1 << vbits))) return TQ_ERR_UNSUPPORTED;
+    if (!tq::score_attend_supported(keys->layout, bits, C, values->layout, vbits, C_v, D)) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0) return TQ_OK;   // empty call: nothing to launch
+    if (S == 0) return TQ_ERR_ARG;        // softmax over no keys
+    if (!A || !T || !codebook || !codebook_v || !Pi_v || !out || !workspace || !values->idx || !values->norm)
+        return TQ_ERR_ARG;
+    kc = check_buffers(keys, P, S, D);
+    if (kc != TQ_OK) return kc;
+    if (S >= kMfmaMaxKeys || B > 262144 || !fits(P, B, S) || !fits(P, B, D)) return TQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < tq_score_attend_workspace_bytes(P, B, S, D)) return TQ_ERR_ARG;
+    if (!aligned16(A) || !aligned16(T) || !aligned16(codebook) || !aligned16(codebook_v) || !aligned16(Pi_v) ||
+        !aligned16(out) || !aligned16(workspace) || !aligned16(values->idx) || !aligned16(values->norm))
+        return TQ_ERR_ALIGN;
+    int chunk = 0, nch = 0;
+    tq::score_attend_plan(P, B, S, chunk, nch);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    const tq::ValueStreams v{static_cast<const uint8_t*>(values->idx), values->norm};
+    hipError_t e = tq::launch_score_attend_partial(A, T, streams(keys), keys->layout, bits, codebook, C, v,
+                                                   values->layout, vbits, codebook_v, C_v, scale, ws, P, B, S, chunk,
+                                                   nch, st);
+    if (e == hipSuccess) e = tq::launch_attend_combine(ws, Pi_v, out, P, H, B, D, nch, st);
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 int tq_query_transform_hadamard(const float* q, const float* signs, float* A, int P, int H, int B, int D,
                                 void* stream) {
     if (P < 0 || H <= 0 || B < 0 || D <= 0 || P % H != 0) return TQ_ERR_ARG;

@@ -578,6 +578,17 @@ hipError_t launch_attend_layout(const float* scores, ValueStreams v, const float
 
 // The unpacked layout reads the most bytes per key, so it has the shortest
 // chunks and the most of them: its count bounds every layout's.
+hipError_t launch_attend_combine(const float* ws, const float* Pi_v, float* out, int P, int H, int B, int D, int nch,
+                                 hipStream_t stream) {
+    if (D == 64)
+        hipLaunchKernelGGL((attend_combine_kernel<64>), dim3((unsigned)B, P), dim3(256), 0, stream, ws, Pi_v, out, H, B, nch);
+    else if (D == 128)
+        hipLaunchKernelGGL((attend_combine_kernel<128>), dim3((unsigned)B, P), dim3(256), 0, stream, ws, Pi_v, out, H, B, nch);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 int attend_chunks(int P, int B, int S, int D) { return make_plan(P, B, S, D, 0, 0).nmax; }
 
 bool attend_supported(int layout, int bits, int C, int D) {

@@ -101,6 +101,18 @@ hipError_t launch_score_split(const float* A_hi, const float* A_lo, SplitStreams
                               const float* cb_hi, int C_hi, const float* cb_lo, int C_lo, float* scores, int P,
                               int B, int S, int D_hi, int D_lo, hipStream_t stream);
 
+// Fused decode step: scores, online softmax and values in one pass
+// (score_mfma.hip), writing the attend workspace records; then the attend
+// combine (attend.hip).
+void score_attend_plan(int P, int B, int S, int& chunk, int& nch);
+bool score_attend_supported(int layout, int bits, int C, int vlayout, int vbits, int VC, int D);
+hipError_t launch_score_attend_partial(const float* A, const float* T, KeyStreams keys, int layout, int bits,
+                                       const float* codebook, int C, ValueStreams v, int vlayout, int vbits,
+                                       const float* vcodebook, int VC, float scale, float* ws, int P, int B, int S,
+                                       int chunk, int nch, hipStream_t stream);
+hipError_t launch_attend_combine(const float* ws, const float* Pi_v, float* out, int P, int H, int B, int D, int nch,
+                                 hipStream_t stream);
+
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                          int P, int S, int D, hipStream_t stream);

@@ -275,6 +275,36 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
               int P, int H, int B, int S, int D, void* stream);
 
 /*
+ * tq_score_attend_workspace_bytes: workspace tq_score_attend needs for this
+ * shape (0 for an empty shape or invalid sizes). Host-only.
+ */
+size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D);
+
+/*
+ * tq_score_attend: the fused decode step, tq_score then tq_attend without
+ * writing the scores: each key tile is scored and immediately folded into an
+ * online softmax and the value sum ("Fitting 4.4x More Context on Jetson",
+ * section "v6: Fused Vectorized Hybrid" and its online-softmax FAQ;
+ * "TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits", section 8). For each
+ * problem p (head h = p % H) and query b:
+ *
+ *   s_t    = the raw score of query b against key t (tq_score's formula)
+ *   out[p,b,:] = Pi_v[h]^T sum_t softmax(scale * s)_t norm[t] codebook_v[idx_v[t,:]]
+ *
+ *   A, T, keys, codebook, C   as for tq_score (C <= 8)
+ *   values, codebook_v, C_v   as for tq_attend (C_v <= 8)
+ *   Pi_v, scale, out          as for tq_attend
+ *   workspace                 at least tq_score_attend_workspace_bytes(P, B, S, D)
+ *
+ * D = 128, S < 2^24. Result within 1e-4 * (1 + |exact|) of the exact output
+ * for the given inputs. Errors as for tq_score and tq_attend.
+ */
+int tq_score_attend(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
+                    const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v, float scale,
+                    float* out, void* workspace, size_t workspace_bytes, int P, int H, int B, int S, int D,
+                    void* stream);
+
+/*
  * tq_query_transform_hadamard: A = H D q for every query, the randomized
  * Hadamard rotation ("TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits",
  * section 2): D = diag(signs) of the query's head, H the orthonormal

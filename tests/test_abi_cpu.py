@@ -13,6 +13,7 @@ EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
     "tq_query_transform_hadamard", "tq_score_mse", "tq_query_transform_split", "tq_score_split",
+    "tq_score_attend", "tq_score_attend_workspace_bytes",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -236,3 +237,23 @@ def test_split_rejects_bad_arguments():
     assert sf(16, 16, keys(lo=inst(bits=2, norm=None)), 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ARG
     assert sf(16, 24, keys(), 16, 8, 16, 4, 16, 1, 4, 8, 32, 96, None) == ALIGN
     assert sf(None, None, keys(), None, 8, None, 4, None, 1, 4, 0, 32, 96, None) == OK
+
+
+def test_score_attend_rejects_bad_arguments():
+    f = tq._lib.tq_score_attend
+    ws = 1 << 30
+    vals = lambda layout=0, bits=0, idx=16, norm=16: ctypes.byref(tq._CValues(layout, bits, idx, norm))
+    k = ctypes.byref(_keys())
+    a = (16, 16)
+    assert f(*a, k, 16, 4, None, 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ARG
+    assert f(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 3, 2, 4, 8, 128, None) == ARG     # P % H
+    assert f(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 0, 128, None) == ARG     # no keys
+    assert f(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, 8, 1, 1, 4, 8, 128, None) == ARG      # workspace
+    assert f(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 64, None) == UNSUP    # D != 128
+    assert f(*a, k, 16, 4, vals(), 16, 16, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == UNSUP  # C_v > 8
+    assert f(*a, k, 16, 16, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == UNSUP  # C > 8
+    assert f(*a, k, 16, 4, vals(layout=1, bits=3), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == UNSUP
+    assert f(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 1 << 24, 128, None) == UNSUP
+    assert f(20, 16, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ALIGN
+    assert f(None, None, k, None, 4, vals(), None, 4, None, 1.0, None, None, 0, 1, 1, 0, 8, 128, None) == OK
+    assert tq.tq_score_attend_workspace_bytes(1, 32, 32768, 128) > 0
