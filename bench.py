@@ -53,13 +53,14 @@ def parse():
                     help="decode (default, the quoted configuration); others for profiling")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
-    ap.add_argument("--path", default="score", choices=["score", "compress", "attend", "mse", "split"],
+    ap.add_argument("--path", default="score", choices=["score", "compress", "attend", "mse", "split", "fused"],
                     help="score (default): the scoring hot path; compress: the key compressor "
                          "(tq_compress_keys) on the workload's key set; attend: softmax and value "
                          "aggregation (tq_attend) over the workload's scores and values; mse: the "
                          "MSE-only variant (tq_query_transform_hadamard + tq_score_mse); split: the "
                          "outlier split, 32 hot channels at 3 bits + the rest at 2 (tq_query_transform_split "
-                         "+ tq_score_split)")
+                         "+ tq_score_split); fused: the whole decode step, tq_query_transform + "
+                         "tq_score_attend (scores never written), against the two-call form")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -737,6 +738,168 @@ def bench_split(args, w, device) -> dict:
     return out
 
 
+def bench_fused(args, w, device) -> dict:
+    """One step = tq_query_transform + tq_score_attend over the workload: its
+    keys, and values in the same layout and codebook size. Timed beside the
+    unfused form (tq_score then tq_attend) on the same inputs; per-kernel times
+    from phased graph replays."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+    import synth
+
+    bits = w.bits if w.layout == "packed" else 0
+    Pi, S_mat = synth.head_matrices(w.seed, w.H, w.D)
+    rng = np.random.default_rng([w.seed, 7])
+    Pi_v = np.stack([synth.haar_rotation(rng, w.D) for _ in range(w.H)])
+    cb = synth.timing_codebook(w.seed, w.C, w.D)
+    cbv = synth.timing_codebook(w.seed + 1, w.C, w.D)
+    q = synth.queries(w.seed, w.P, w.B, w.D)
+    idx, sign, gamma = synth.timing_code_streams(w.seed, w.P, w.S, w.D, w.C, w.layout, w.bits)
+    vidx, vnorm = synth.timing_value_streams(w.seed, w.P, w.S, w.D, w.C, w.layout, bits)
+    shared = {k: torch.from_numpy(v).to(device) for k, v in
+              {"Pi": Pi, "S_mat": S_mat, "Pi_v": Pi_v, "cb": cb, "cbv": cbv}.items()}
+    base = {k: torch.from_numpy(v).to(device) for k, v in
+            {"q": q, "idx": idx, "sign": sign, "gamma": gamma, "vidx": vidx, "vnorm": vnorm}.items()}
+    per_set = w.key_bytes() + base["vidx"].numel() + base["vnorm"].numel() * base["vnorm"].element_size()
+    nsets = max(2, min(64, math.ceil(RING_BYTES / per_set)))
+    wsf = tq.tq_score_attend_workspace_bytes(w.P, w.B, w.S, w.D, "fused")
+    wsa = tq.tq_attend_workspace_bytes(w.P, w.B, w.S, w.D)
+    ring = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in base.items()}
+        s["keys"] = tq.Keys(w.layout, s["idx"], s["sign"], s["gamma"], bits)
+        s["values"] = tq.Values(w.layout, s["vidx"], s["vnorm"], bits)
+        s["A"] = torch.empty((w.P, w.B, w.D), dtype=torch.float32, device=device)
+        s["T"] = torch.empty_like(s["A"])
+        s["out"] = torch.empty_like(s["A"])
+        ring.append(s)
+    ws_f = torch.empty(wsf, dtype=torch.uint8, device=device)     # calls on one stream run in order
+    ws_auto = torch.empty(tq.tq_score_attend_workspace_bytes(w.P, w.B, w.S, w.D), dtype=torch.uint8, device=device)
+    ws_a = torch.empty(wsa, dtype=torch.uint8, device=device)
+    scores = torch.empty((w.P, w.B, w.S), dtype=torch.float32, device=device)
+    scale = 1.0 / math.sqrt(w.D)
+
+    def transform(s):
+        tq.tq_query_transform(s["q"], shared["Pi"], shared["S_mat"], s["A"], s["T"])
+
+    def fused(s):
+        tq.tq_score_attend(s["A"], s["T"], s["keys"], shared["cb"], s["values"], shared["cbv"], shared["Pi_v"],
+                           scale, s["out"], ws_f, mode="fused")
+
+    def automatic(s):
+        tq.tq_score_attend(s["A"], s["T"], s["keys"], shared["cb"], s["values"], shared["cbv"], shared["Pi_v"],
+                           scale, s["out"], ws_auto)
+
+    def unfused(s):
+        tq.tq_score(s["A"], s["T"], s["keys"], shared["cb"], scores)
+        tq.tq_attend(scores, s["values"], shared["cbv"], shared["Pi_v"], scale, s["out"], ws_a)
+
+    for i in range(args.warmup):
+        transform(ring[i % nsets])
+        fused(ring[i % nsets])
+        unfused(ring[i % nsets])
+        automatic(ring[i % nsets])
+    torch.cuda.synchronize()
+    steps = args.steps
+    chunks = [nsets] * (steps // nsets) + ([steps % nsets] if steps % nsets else [])
+
+    def phased(second):
+        graphs = {}
+        for n in sorted(set(chunks)):
+            g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1):
+                for i in range(n):
+                    transform(ring[i])
+            with torch.cuda.graph(g2):
+                for i in range(n):
+                    second(ring[i])
+            graphs[n] = (g1, g2)
+        for g1, g2 in graphs.values():
+            g1.replay()
+            g2.replay()
+        torch.cuda.synchronize()
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in chunks]
+        t0 = time.perf_counter()
+        for n, ev in zip(chunks, evs):
+            g1, g2 = graphs[n]
+            ev[0].record()
+            g1.replay()
+            ev[1].record()
+            g2.replay()
+            ev[2].record()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        return (el, 1e3 * sum(a.elapsed_time(b) for a, b, _ in evs) / steps,
+                1e3 * sum(b.elapsed_time(c) for _, b, c in evs) / steps)
+
+    el_a, qt_us, auto_us = phased(automatic)
+    _, _, fused_us = phased(fused)
+    el_u, _, unfused_us = phased(unfused)
+    if w.layout == "unpacked":
+        vb = w.D + 4
+    else:
+        vb = w.D * w.bits // 8 + 2
+    nbytes = w.key_bytes() + w.P * w.S * vb + 2 * w.P * w.B * w.D * 4 + 2 * w.C * 4 + w.H * w.D * w.D * 4 \
+        + w.P * w.B * w.D * 4
+    achieved = nbytes / (fused_us * 1e-6) / 1e9
+    ms_per_step = el_a * 1e3 / steps
+    log(f"fused: transform {qt_us:.2f} us, tq_score_attend {auto_us:.2f} us per call (one-pass form "
+        f"{fused_us:.2f}, score then attend {unfused_us:.2f}); one-pass {achieved:.0f} GB/s algorithmic")
+    out = {
+        "metric": "decode steps/sec (query transform + tq_score_attend: scores, softmax and value sum)",
+        "value": w.P * w.B / (ms_per_step * 1e-3),
+        "unit": "query outputs/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate",
+        "data": "synthetic: seeded random key and value codes, N(0,1) queries, Haar rotations, Gaussian projection",
+        "config": {"workload": w.name, "path": "fused", "P": w.P, "H": w.H, "B": w.B, "S": w.S, "D": w.D, "C": w.C,
+                   "layout": w.layout, "bits": w.bits, "scale": scale},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "score_attend_kernel + attend_combine", "bytes_per_launch": nbytes,
+                     "avg_launch_us": fused_us, "workspace_bytes": wsf},
+        "tq_score_attend_us": auto_us,
+        "one_pass_form_us": fused_us,
+        "unfused_score_then_attend_us": unfused_us,
+        "ms_per_step_unfused": el_u * 1e3 / steps,
+        "tq_query_transform_us": qt_us,
+        "ring_sets": nsets,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import attend as oa
+        from oracle import score as osc
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from oracle import pack as opk
+        if w.layout == "unpacked":
+            iu, su, vu = idx[0], sign[0], vidx[0]
+        else:
+            iu, su = opk.unpack_indices(idx[0], w.bits, w.D), opk.unpack_signs(sign[0], w.D)
+            vu = opk.unpack_indices(vidx[0], w.bits, w.D)
+        times = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < args.cpu_seconds or len(times) < 3:
+            t1 = time.perf_counter()
+            sco = osc.scores_by_reconstruction(q[0], iu, su, gamma[0].astype(np.float64), Pi[0], S_mat[0], cb)
+            oa.attend_rotated(sco, vu, vnorm[0].astype(np.float64), Pi_v[0], cbv, scale)
+            times.append(time.perf_counter() - t1)
+        med = sorted(times)[len(times) // 2]
+        out["cpu_baseline"] = {"value": w.B / med, "unit": "query outputs/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"problem 0 (B={w.B}, S={w.S}, D={w.D}): float64 scores by reconstruction, "
+                                         f"then softmax and value sum, median of {len(times)} runs "
+                                         f"({sum(times):.1f} s total)"}
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -766,6 +929,9 @@ def main() -> int:
         return 0
     if args.path == "split":
         print(json.dumps(bench_split(args, w, device)), flush=True)
+        return 0
+    if args.path == "fused":
+        print(json.dumps(bench_fused(args, w, device)), flush=True)
         return 0
     kname = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, args.kernel)
     log(f"workload {w.describe()} kernel {kname}")

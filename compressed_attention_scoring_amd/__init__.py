@@ -109,11 +109,15 @@ def _load():
     lib.tq_attend.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp, vp, ctypes.c_size_t,
                               i32, i32, i32, i32, i32, vp]
     lib.tq_attend.restype = i32
-    lib.tq_score_attend_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.tq_score_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.tq_score_attend_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_score_attend.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, ctypes.POINTER(_CValues), vp, i32, vp,
                                     ctypes.c_float, vp, vp, ctypes.c_size_t, i32, i32, i32, i32, i32, vp]
     lib.tq_score_attend.restype = i32
+    lib.tq_score_attend_with_mode.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, ctypes.POINTER(_CValues), vp,
+                                              i32, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, i32, i32, i32, i32,
+                                              i32, i32, vp]
+    lib.tq_score_attend_with_mode.restype = i32
     lib.tq_query_transform_hadamard.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     lib.tq_query_transform_hadamard.restype = i32
     lib.tq_score_mse.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, i32, i32, i32, i32, vp]
@@ -518,17 +522,20 @@ def tq_score_split(A_hi: torch.Tensor, A_lo: torch.Tensor, keys: SplitKeys, code
     return scores.view(P, B, S)
 
 
-def tq_score_attend_workspace_bytes(P: int, B: int, S: int, D: int) -> int:
-    """Workspace bytes tq_score_attend needs for this shape."""
-    return int(_lib.tq_score_attend_workspace_bytes(int(P), int(B), int(S), int(D)))
+ATTEND_MODES = {"auto": 0, "fused": 1, "two_pass": 2}
+
+
+def tq_score_attend_workspace_bytes(P: int, B: int, S: int, D: int, mode: str = "auto") -> int:
+    """Workspace bytes tq_score_attend needs for this shape and form."""
+    return int(_lib.tq_score_attend_workspace_bytes(int(P), int(B), int(S), int(D), ATTEND_MODES[mode]))
 
 
 def tq_score_attend(A: torch.Tensor, T: torch.Tensor, keys: Keys, codebook: torch.Tensor, values: Values,
                     codebook_v: torch.Tensor, Pi_v: torch.Tensor, scale: float | None = None,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
-    """The fused decode step: softmax(scale * scores) times the dequantized values,
-    without writing the scores. out [P,B,D]."""
+                    stream=None, mode: str = "auto") -> torch.Tensor:
+    """The fused decode step: softmax(scale * scores) times the dequantized values.
+    out [P,B,D]. mode: "auto", "fused" (scores never written) or "two_pass"."""
     A3 = _as3(_gpu(A, "A", torch.float32))
     T3 = _as3(_gpu(T, "T", torch.float32))
     _gpu(codebook, "codebook", torch.float32)
@@ -550,12 +557,12 @@ def tq_score_attend(A: torch.Tensor, T: torch.Tensor, keys: Keys, codebook: torc
     _gpu(out, "out", torch.float32)
     if out.numel() != P * B * D:
         raise ValueError("out must hold P*B*D floats")
-    need = tq_score_attend_workspace_bytes(P, B, S, D)
+    need = tq_score_attend_workspace_bytes(P, B, S, D, mode)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _gpu(workspace, "workspace", torch.uint8)
-    _check(_lib.tq_score_attend(_ptr(A3), _ptr(T3), ctypes.byref(ck), _ptr(codebook), codebook.numel(),
-                                ctypes.byref(cv), _ptr(codebook_v), codebook_v.numel(), _ptr(Pv), float(scale),
-                                _ptr(out), _ptr(workspace), workspace.numel(), P, H, B, S, D, _stream(dev, stream)),
-           "tq_score_attend")
+    _check(_lib.tq_score_attend_with_mode(_ptr(A3), _ptr(T3), ctypes.byref(ck), _ptr(codebook), codebook.numel(),
+                                          ctypes.byref(cv), _ptr(codebook_v), codebook_v.numel(), _ptr(Pv),
+                                          float(scale), _ptr(out), _ptr(workspace), workspace.numel(), P, H, B, S, D,
+                                          ATTEND_MODES[mode], _stream(dev, stream)), "tq_score_attend")
     return out.view(P, B, D)

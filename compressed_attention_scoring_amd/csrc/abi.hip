@@ -204,18 +204,37 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
-size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D) {
-    if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
-    int chunk = 0, nch = 0;
+namespace {
+// tq_score_attend runs fused when every wavefront of the fused kernel gets at
+// least two 32-key tiles and the query tile is not mostly padding; otherwise as
+// two passes with the scores in the workspace. Measured (us per call, fused /
+// two passes): B=32 S=131072 31 / 41, B=128 S=262144 118 / 141, B=32 S=32768
+// 22.5 / 20.5, P=128 B=4 404 / 255.
+bool fused_step(int P, int B, int S, int& chunk, int& nch) {
     tq::score_attend_plan(P, B, S, chunk, nch);
-    return (size_t)((int64_t)P * B * nch * (D + 2) * (int64_t)sizeof(float));
+    return B > 8 && chunk >= 8 * 32;
 }
 
-int tq_score_attend(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
-                    const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v, float scale,
-                    float* out, void* workspace, size_t workspace_bytes, int P, int H, int B, int S, int D,
-                    void* stream) {
+int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+}  // namespace
+
+size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D, int mode) {
+    if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
+    if (mode != TQ_ATTEND_AUTO && mode != TQ_ATTEND_FUSED && mode != TQ_ATTEND_TWO_PASS) return 0;
+    int chunk = 0, nch = 0;
+    const bool fused = fused_step(P, B, S, chunk, nch);
+    if (mode == TQ_ATTEND_FUSED || (mode == TQ_ATTEND_AUTO && fused))
+        return (size_t)((int64_t)P * B * nch * (D + 2) * (int64_t)sizeof(float));
+    return (size_t)(align256((int64_t)P * B * S * (int64_t)sizeof(float)) +
+                    (int64_t)tq_attend_workspace_bytes(P, B, S, D));
+}
+
+int tq_score_attend_with_mode(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
+                              const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v,
+                              float scale, float* out, void* workspace, size_t workspace_bytes, int P, int H, int B,
+                              int S, int D, int mode, void* stream) {
     if (!values || P < 0 || B < 0 || S < 0 || H <= 0 || P % H != 0) return TQ_ERR_ARG;
+    if (mode != TQ_ATTEND_AUTO && mode != TQ_ATTEND_FUSED && mode != TQ_ATTEND_TWO_PASS) return TQ_ERR_ARG;
     int kc = check_format(keys, C, D, true);
     if (kc != TQ_OK) return kc;
     if (values->layout != TQ_UNPACKED && values->layout != TQ_PACKED) return TQ_ERR_ARG;
@@ -230,20 +249,40 @@ int tq_score_attend(const float* A, const float* T, const tq_keys* keys, const f
     kc = check_buffers(keys, P, S, D);
     if (kc != TQ_OK) return kc;
     if (S >= kMfmaMaxKeys || B > 262144 || !fits(P, B, S) || !fits(P, B, D)) return TQ_ERR_UNSUPPORTED;
-    if (workspace_bytes < tq_score_attend_workspace_bytes(P, B, S, D)) return TQ_ERR_ARG;
+    if (workspace_bytes < tq_score_attend_workspace_bytes(P, B, S, D, mode)) return TQ_ERR_ARG;
     if (!aligned16(A) || !aligned16(T) || !aligned16(codebook) || !aligned16(codebook_v) || !aligned16(Pi_v) ||
         !aligned16(out) || !aligned16(workspace) || !aligned16(values->idx) || !aligned16(values->norm))
         return TQ_ERR_ALIGN;
     int chunk = 0, nch = 0;
-    tq::score_attend_plan(P, B, S, chunk, nch);
+    const bool auto_fused = fused_step(P, B, S, chunk, nch);
+    const bool fused = mode == TQ_ATTEND_FUSED || (mode == TQ_ATTEND_AUTO && auto_fused);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float* ws = static_cast<float*>(workspace);
     const tq::ValueStreams v{static_cast<const uint8_t*>(values->idx), values->norm};
-    hipError_t e = tq::launch_score_attend_partial(A, T, streams(keys), keys->layout, bits, codebook, C, v,
-                                                   values->layout, vbits, codebook_v, C_v, scale, ws, P, B, S, chunk,
-                                                   nch, st);
-    if (e == hipSuccess) e = tq::launch_attend_combine(ws, Pi_v, out, P, H, B, D, nch, st);
+    hipError_t e;
+    if (fused) {
+        e = tq::launch_score_attend_partial(A, T, streams(keys), keys->layout, bits, codebook, C, v, values->layout,
+                                            vbits, codebook_v, C_v, scale, ws, P, B, S, chunk, nch, st);
+        if (e == hipSuccess) e = tq::launch_attend_combine(ws, Pi_v, out, P, H, B, D, nch, st);
+    } else {
+        float* scores = ws;
+        float* aws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
+                                              align256((int64_t)P * B * S * (int64_t)sizeof(float)));
+        e = tq::launch_score_mfma(A, T, streams(keys), keys->layout, bits, codebook, C, scores, P, B, S, D,
+                                  tq::kMfmaAuto, st);
+        if (e == hipSuccess)
+            e = tq::launch_attend(scores, v, values->layout, vbits, codebook_v, C_v, Pi_v, scale, out, aws, P, H, B,
+                                  S, D, st);
+    }
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_score_attend(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
+                    const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v, float scale,
+                    float* out, void* workspace, size_t workspace_bytes, int P, int H, int B, int S, int D,
+                    void* stream) {
+    return tq_score_attend_with_mode(A, T, keys, codebook, C, values, codebook_v, C_v, Pi_v, scale, out, workspace,
+                                     workspace_bytes, P, H, B, S, D, TQ_ATTEND_AUTO, stream);
 }
 
 int tq_query_transform_hadamard(const float* q, const float* signs, float* A, int P, int H, int B, int D,

@@ -274,11 +274,17 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
               const float* Pi_v, float scale, float* out, void* workspace, size_t workspace_bytes,
               int P, int H, int B, int S, int D, void* stream);
 
+/* forms of the fused decode step; TQ_ATTEND_AUTO picks by shape */
+#define TQ_ATTEND_AUTO     0
+#define TQ_ATTEND_FUSED    1  /* one pass: scores never written */
+#define TQ_ATTEND_TWO_PASS 2  /* scores into the workspace, then softmax and values */
+
 /*
- * tq_score_attend_workspace_bytes: workspace tq_score_attend needs for this
- * shape (0 for an empty shape or invalid sizes). Host-only.
+ * tq_score_attend_workspace_bytes: workspace tq_score_attend_with_mode needs
+ * for this shape and form (0 for an empty shape, invalid sizes or an unknown
+ * form). Host-only.
  */
-size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D);
+size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D, int mode);
 
 /*
  * tq_score_attend: the fused decode step, tq_score then tq_attend without
@@ -296,6 +302,14 @@ size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D);
  *   Pi_v, scale, out          as for tq_attend
  *   workspace                 at least tq_score_attend_workspace_bytes(P, B, S, D)
  *
+ * The call runs fused (one pass over keys and values, scores never written)
+ * when every wavefront of the fused kernel gets at least two 32-key tiles and
+ * B > 8; otherwise, where the two-pass form measured faster (short key chunks,
+ * a few queries per problem), it writes the scores into the workspace and runs
+ * tq_score and tq_attend's kernels. tq_score_attend_with_mode forces a form.
+ * The workspace is tq_score_attend_workspace_bytes(P, B, S, D, mode) bytes for
+ * the form used (TQ_ATTEND_AUTO for tq_score_attend).
+ *
  * D = 128, S < 2^24. Result within 1e-4 * (1 + |exact|) of the exact output
  * for the given inputs. Errors as for tq_score and tq_attend.
  */
@@ -303,6 +317,12 @@ int tq_score_attend(const float* A, const float* T, const tq_keys* keys, const f
                     const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v, float scale,
                     float* out, void* workspace, size_t workspace_bytes, int P, int H, int B, int S, int D,
                     void* stream);
+
+/* tq_score_attend with an explicit form (TQ_ATTEND_*), so that both forms can be checked on every shape. */
+int tq_score_attend_with_mode(const float* A, const float* T, const tq_keys* keys, const float* codebook, int C,
+                              const tq_values* values, const float* codebook_v, int C_v, const float* Pi_v,
+                              float scale, float* out, void* workspace, size_t workspace_bytes, int P, int H, int B,
+                              int S, int D, int mode, void* stream);
 
 /*
  * tq_query_transform_hadamard: A = H D q for every query, the randomized

@@ -13,7 +13,7 @@ EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
     "tq_query_transform_hadamard", "tq_score_mse", "tq_query_transform_split", "tq_score_split",
-    "tq_score_attend", "tq_score_attend_workspace_bytes",
+    "tq_score_attend", "tq_score_attend_workspace_bytes", "tq_score_attend_with_mode",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -256,4 +256,11 @@ def test_score_attend_rejects_bad_arguments():
     assert f(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 1 << 24, 128, None) == UNSUP
     assert f(20, 16, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, None) == ALIGN
     assert f(None, None, k, None, 4, vals(), None, 4, None, 1.0, None, None, 0, 1, 1, 0, 8, 128, None) == OK
-    assert tq.tq_score_attend_workspace_bytes(1, 32, 32768, 128) > 0
+    for mode in ("auto", "fused", "two_pass"):
+        assert tq.tq_score_attend_workspace_bytes(1, 32, 32768, 128, mode) > 0
+    # two passes hold the scores; the fused form only the chunk records
+    assert tq.tq_score_attend_workspace_bytes(1, 128, 262144, 128, "two_pass") > 128 * 262144 * 4
+    assert tq.tq_score_attend_workspace_bytes(1, 128, 262144, 128, "fused") < 128 * 262144 * 4 / 16
+    assert tq._lib.tq_score_attend_workspace_bytes(1, 32, 100, 128, 7) == 0
+    g = tq._lib.tq_score_attend_with_mode
+    assert g(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, 3, None) == ARG    # unknown form

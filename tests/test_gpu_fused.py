@@ -1,4 +1,5 @@
-"""tq_score_attend (the fused decode step) against the oracle chain: oracle
+"""tq_score_attend (the fused decode step), in both its forms and the automatic
+choice, against the oracle chain: oracle
 scores from the fp32 A, T the GPU is given (oracle.score), then the oracle's
 softmax and value sum (oracle.attend). Key and value layouts, ragged query
 and key counts, several problems and heads, and each workload's full size.
@@ -33,7 +34,7 @@ def values_case(rng, P, H, S, C, layout, bits):
     return tq.Values("packed", t(opk.pack_indices(idx, bits)), t(n), bits), idx, n.astype(np.float64), Pi_v, cb
 
 
-def run(seed, P, H, B, S, key_fmt, val_fmt, scale):
+def run(seed, P, H, B, S, key_fmt, val_fmt, scale, modes=("fused", "two_pass", "auto")):
     rng = np.random.default_rng(seed)
     klay, kbits, kC = key_fmt
     vlay, vbits, vC = val_fmt
@@ -43,13 +44,13 @@ def run(seed, P, H, B, S, key_fmt, val_fmt, scale):
     A = (rng.standard_normal((P, B, D)) * 0.5).astype(np.float32)
     Tq = (rng.standard_normal((P, B, D)) * 0.5).astype(np.float32)
     vals, vidx, vnorm, Pi_v, cbv = values_case(rng, P, H, S, vC, vlay, vbits)
-    got = tq.tq_score_attend(t(A), t(Tq), keys, t(cbk), vals, t(cbv), t(Pi_v), scale).cpu().numpy()
     scores = oracle_scores_transformed(A, Tq, idx_u, sign_u, gamma, cbk)
     ref = np.stack([oa.attend_rotated(scores[p], vidx[p], vnorm[p], Pi_v[p % H].astype(np.float64),
                                       cbv.astype(np.float64), scale) for p in range(P)])
-    err = rel_err(got, ref)
-    assert err <= SCORE_TOL, f"max rel err {err:.3e}"
-    return got
+    for mode in modes:
+        got = tq.tq_score_attend(t(A), t(Tq), keys, t(cbk), vals, t(cbv), t(Pi_v), scale, mode=mode).cpu().numpy()
+        err = rel_err(got, ref)
+        assert err <= SCORE_TOL, f"{mode}: max rel err {err:.3e}"
 
 
 KEY_FMTS = [("unpacked", 0, 4), ("packed", 2, 4), ("packed", 3, 8)]
@@ -87,7 +88,7 @@ def test_fused_matches_two_calls():
     A = rng.standard_normal((P, B, D)).astype(np.float32)
     Tq = rng.standard_normal((P, B, D)).astype(np.float32)
     vals, vidx, vnorm, Pi_v, cbv = values_case(rng, P, H, S, 4, "packed", 2)
-    fused = tq.tq_score_attend(t(A), t(Tq), keys, t(cbk), vals, t(cbv), t(Pi_v), 0.3).cpu().numpy()
+    fused = tq.tq_score_attend(t(A), t(Tq), keys, t(cbk), vals, t(cbv), t(Pi_v), 0.3, mode="fused").cpu().numpy()
     sc = tq.tq_score(t(A), t(Tq), keys, t(cbk))
     two = tq.tq_attend(sc, vals, t(cbv), t(Pi_v), 0.3).cpu().numpy()
     assert rel_err(fused, two) <= 2 * SCORE_TOL
