@@ -1063,19 +1063,23 @@ struct SmallFmt {
     static constexpr int NJ = Q / 8;                           // k-steps of 8 coordinates per lane
 };
 
-template <int LAYOUT, int BITS, int D>
+template <int LAYOUT, int BITS, int D, bool QJL = true>
 __device__ __forceinline__ void load_quarter(TileCodes<SmallFmt<LAYOUT, BITS, D>::NI, SmallFmt<LAYOUT, BITS, D>::NS>& c,
                                              const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
                                              const void* __restrict__ gamma, int64_t key, int gq) {
     using SF = SmallFmt<LAYOUT, BITS, D>;
     constexpr int IQ = SF::IDX_ROW / 4, SQ = SF::SIGN_ROW / 4;
     load_dwords<SF::NI, align_of_seg(SF::IDX_ROW, IQ)>(idx + key * SF::IDX_ROW + gq * IQ, c.iw);
-    load_dwords<SF::NS, align_of_seg(SF::SIGN_ROW, SQ)>(sign + key * SF::SIGN_ROW + gq * SQ, c.sw);
+    if constexpr (QJL) load_dwords<SF::NS, align_of_seg(SF::SIGN_ROW, SQ)>(sign + key * SF::SIGN_ROW + gq * SQ, c.sw);
     if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
     else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
 }
 
-template <int LAYOUT, int BITS, int D, int MINW>
+// QJL = false (MSE-only keys, gamma = the key's norm, no sign stream): row
+// types 0 and 1 stay A_hi and A_lo against the codebook's hi part in elements
+// 0-3, type 2 is A_hi against its lo part in elements 4-7, type 3 is zero, so
+// two MFMAs per k-step cover what takes three with signs.
+template <int LAYOUT, int BITS, int D, int MINW, bool QJL = true>
 __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
@@ -1102,7 +1106,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
 
     // this lane's quarter row: A for types 0-1, T for types 2-3 (query rb,
     // clamped: queries past B are computed but never stored)
-    const float* src = (rtype < 2 ? A : T) + ((int64_t)p * B + b0 + min(rb, nb - 1)) * D + gq * Q;
+    const float* src = (rtype < 2 || !QJL ? A : T) + ((int64_t)p * B + b0 + min(rb, nb - 1)) * D + gq * Q;
     float x[Q];
 #pragma unroll
     for (int k = 0; k < Q; k += 4) {
@@ -1111,7 +1115,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     }
     TileCodes<NI, NS> cur;
     asm volatile("" ::: "memory");
-    load_quarter<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
+    load_quarter<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
     asm volatile("" ::: "memory");
     float sc;
     uint32_t tab_hi[4], tab_lo[4];
@@ -1135,7 +1139,8 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     // (coordinates mse_dim(j, 0..3) and (j, 4..7)) with sign elements 4-7
     // (coordinates qjl_dim(j, 0..3) and (j, 4..7)); ops[j][2] is A_hi over
     // mse_dim(j, 0..7) for the codebook-lo product.
-    Op8 ops[NJ][3];
+    constexpr int NO = QJL ? 3 : 2;
+    Op8 ops[NJ][NO];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -1145,17 +1150,23 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
                 const float xa = x[mse_dim<LAYOUT, BITS>(j, 4 * h + e)] * s_row;
                 const _Float16 ha = (_Float16)xa;
                 const _Float16 la = (_Float16)(xa - (float)ha);
-                const float xt = x[qjl_dim<LAYOUT>(j, 4 * h + e)] * s_row;
-                const _Float16 ht = (_Float16)xt;
-                const _Float16 lt = (_Float16)(xt - (float)ht);
                 ops[j][h].h[e] = rtype == 0 ? ha : rtype == 1 ? la : (_Float16)0.f;
-                ops[j][h].h[4 + e] = rtype == 2 ? ht : rtype == 3 ? lt : (_Float16)0.f;
+                if constexpr (QJL) {
+                    const float xt = x[qjl_dim<LAYOUT>(j, 4 * h + e)] * s_row;
+                    const _Float16 ht = (_Float16)xt;
+                    const _Float16 lt = (_Float16)(xt - (float)ht);
+                    ops[j][h].h[4 + e] = rtype == 2 ? ht : rtype == 3 ? lt : (_Float16)0.f;
+                } else {
+                    ops[j][h].h[4 + e] = rtype == 2 ? ha : (_Float16)0.f;
+                }
             }
         }
+        if constexpr (QJL) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xa = x[mse_dim<LAYOUT, BITS>(j, e)] * s_row;
-            ops[j][2].h[e] = rtype == 0 ? (_Float16)xa : (_Float16)0.f;
+            for (int e = 0; e < 8; ++e) {
+                const float xa = x[mse_dim<LAYOUT, BITS>(j, e)] * s_row;
+                ops[j][NO - 1].h[e] = rtype == 0 ? (_Float16)xa : (_Float16)0.f;
+            }
         }
     }
 
@@ -1167,34 +1178,45 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
         for (int j = 0; j < NJ; ++j) {
             uint32_t x0, x1;
             F::template selectors<NI>(c.iw, j, x0, x1);
-            uint32_t sgn[4];
-            F::template signs<NS>(c.sw, j, sgn);
-            Op8 k0, k1, kl;
+            Op8 k0, k1;
             lut4(x0, tab_hi, k0.u[0], k0.u[1]);
-            k0.u[2] = sgn[0]; k0.u[3] = sgn[1];
             lut4(x1, tab_hi, k1.u[0], k1.u[1]);
-            k1.u[2] = sgn[2]; k1.u[3] = sgn[3];
-            lut4(x0, tab_lo, kl.u[0], kl.u[1]);
-            lut4(x1, tab_lo, kl.u[2], kl.u[3]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][0].h, k0.h, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][1].h, k1.h, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][2].h, kl.h, acc, 0, 0, 0);
+            if constexpr (QJL) {
+                uint32_t sgn[4];
+                F::template signs<NS>(c.sw, j, sgn);
+                Op8 kl;
+                k0.u[2] = sgn[0]; k0.u[3] = sgn[1];
+                k1.u[2] = sgn[2]; k1.u[3] = sgn[3];
+                lut4(x0, tab_lo, kl.u[0], kl.u[1]);
+                lut4(x1, tab_lo, kl.u[2], kl.u[3]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][0].h, k0.h, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][1].h, k1.h, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][2].h, kl.h, acc, 0, 0, 0);
+            } else {
+                lut4(x0, tab_lo, k0.u[2], k0.u[3]);
+                lut4(x1, tab_lo, k1.u[2], k1.u[3]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][0].h, k0.h, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][1].h, k1.h, acc, 0, 0, 0);
+            }
         }
         // lane 16 b + key holds rows 4 b .. 4 b + 3 of column key: the four types
         const int s = t * kTileKeys16 + kc;
         const uint32_t off = s < S ? ((uint32_t)gq * (uint32_t)S + (uint32_t)s) * 4u : kDropKey;
-        store_score(out_r, off, fmaf(ky * c.gam, acc[2] + acc[3], kx * (acc[0] + acc[1])));
+        if constexpr (QJL)
+            store_score(out_r, off, fmaf(ky * c.gam, acc[2] + acc[3], kx * (acc[0] + acc[1])));
+        else
+            store_score(out_r, off, (kx * c.gam) * ((acc[0] + acc[1]) + acc[2]));
     };
 
     TileCodes<NI, NS> nxt;
     while (true) {
-        load_quarter<LAYOUT, BITS, D>(nxt, idx, sign, gamma,
-                                      key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
+        load_quarter<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
+                                           key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
         tile_scores(cur, tile);
         tile += stride;
         if (tile >= ntiles) break;
-        load_quarter<LAYOUT, BITS, D>(cur, idx, sign, gamma,
-                                      key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
+        load_quarter<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma,
+                                           key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
         tile_scores(nxt, tile);
         tile += stride;
         if (tile >= ntiles) break;
@@ -1657,7 +1679,7 @@ hipError_t launch_qs_d(const float* A, const float* T, KeyStreams k, const float
 // Small-batch launch: workgroup rows are groups of four queries; MINW
 // wavefronts per SIMD are resident (the kernel needs about 100 registers at
 // D = 128), so 256 * MINW workgroups fill the chip.
-template <int LAYOUT, int BITS, int D>
+template <int LAYOUT, int BITS, int D, bool QJL = true>
 hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                           float* scores, int P, int B, int S, hipStream_t stream) {
     constexpr int MINW = D <= 128 ? 4 : 2;
@@ -1668,17 +1690,17 @@ hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const fl
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_mfma16_kernel<LAYOUT, BITS, D, MINW>), dim3((unsigned)gx, groups_y, P),
+    hipLaunchKernelGGL((score_mfma16_kernel<LAYOUT, BITS, D, MINW, QJL>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();
 }
 
-template <int LAYOUT, int BITS>
+template <int LAYOUT, int BITS, bool QJL = true>
 hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                                int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
-    if (D == 128) return launch_small_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (D == 256) return launch_small_d<LAYOUT, BITS, 256>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 128) return launch_small_d<LAYOUT, BITS, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 256) return launch_small_d<LAYOUT, BITS, 256, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
     return hipErrorInvalidValue;
 }
 
@@ -1910,6 +1932,12 @@ hipError_t launch_score_mse(const float* A, const uint8_t* idx, const void* norm
                             hipStream_t stream) {
     if (!score_mse_supported(layout, bits, C, D)) return hipErrorInvalidValue;
     const KeyStreams k{idx, nullptr, norm};
+    // one group of four queries over many keys: the 16x16 tiles (as for tq_score)
+    if (pick_variant(layout, bits, C, B, (int64_t)P * S, D) == kMfmaSmall) {
+        if (layout == 0) return launch_small_layout<0, 0, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+        if (bits == 2) return launch_small_layout<1, 2, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+        return launch_small_layout<1, 3, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+    }
     if (layout == 0) return launch_layout<0, 0, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
     if (bits == 2) return launch_layout<1, 2, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
     return launch_layout<1, 3, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);

@@ -115,6 +115,31 @@ def test_score_mse_norm_extremes():
     assert np.max(np.abs(got[0] - ref) / np.maximum(scale, rho[0].astype(np.float64)[None, :])) <= SCORE_TOL
 
 
+@pytest.mark.parametrize("layout,bits,C,D", [("unpacked", 0, 4, 128), ("packed", 2, 4, 128),
+                                              ("packed", 3, 8, 128), ("unpacked", 0, 8, 256)])
+@pytest.mark.parametrize("B", [1, 3, 4])
+def test_score_mse_small_batch_many_keys(layout, bits, C, D, B):
+    """Up to four queries over a million keys or more (the 16x16-tile form):
+    random codes and norms, a ragged key count, every score checked."""
+    say(f"score_mse 16x16 tiles {layout} bits={bits} C={C} D={D} B={B}")
+    P, S = 8, 131075
+    rng = np.random.default_rng([D, B, C, 14])
+    idx = rng.integers(0, C, size=(P, S, D), dtype=np.uint8)
+    rho = rng.uniform(0.5, 2.0, size=(P, S))
+    cb = codebook_fp32(D, C)
+    if layout == "unpacked":
+        r = rho.astype(np.float32)
+        keys = tq.Values("unpacked", t(idx), t(r))
+    else:
+        r = opk.gamma_to_half(rho)
+        keys = tq.Values("packed", t(opk.pack_indices(idx, bits)), t(r), bits)
+    A = synth.queries(B + D, P, B, D) * 3.0
+    got = tq.tq_score_mse(t(A), keys, t(cb)).cpu().numpy()
+    for p in range(P):
+        ref = om.scores_mse_from_transformed(A[p].astype(np.float64), idx[p], r[p].astype(np.float64), cb)
+        assert rel_err(got[p], ref) <= SCORE_TOL
+
+
 @pytest.mark.parametrize("name", ["decode", "packed", "gqa", "long"])
 def test_score_mse_workload_sizes(name):
     """Each workload's shape with MSE-only keys in its layout: full scores for the
