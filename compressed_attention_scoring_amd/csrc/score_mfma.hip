@@ -867,45 +867,49 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
 // workgroup barrier per tile. This removes the fourfold key decoding of the
 // register variant, whose main loop was bound by vector-ALU issue.
 // ---------------------------------------------------------------------------
-template <int LAYOUT, int BITS, int D>
+template <int LAYOUT, int BITS, int D, bool QJL = true>
 struct SharedLds {
     static constexpr int KS = D / 16;
     static constexpr int BLOCK = 64 * 16;                       // one operand: 64 lanes x 16 bytes
-    static constexpr int BUF = KS * 3 * BLOCK;                  // chi, clo, sg of every k-step
+    static constexpr int NB = QJL ? 3 : 2;                      // operands per k-step
+    static constexpr int BUF = KS * NB * BLOCK;                 // chi, clo (and sg) of every k-step
 };
 
-template <int LAYOUT, int BITS, int D, int W>
+template <int LAYOUT, int BITS, int D, int W, bool QJL = true>
 __device__ __forceinline__ void decode_share(const TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
                                                          Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
                                              const uint32_t (&tab_hi)[4], const uint32_t (&tab_lo)[4],
                                              uint8_t* buf, int lane) {
     using F = Fmt<LAYOUT, BITS>;
     constexpr int NI = F::template idx_dw<D>(), NS = F::template sign_dw<D>();
-    constexpr int KS = D / 16, JW = KS / kWaves, BLOCK = SharedLds<LAYOUT, BITS, D>::BLOCK;
+    using L = SharedLds<LAYOUT, BITS, D, QJL>;
+    constexpr int KS = D / 16, JW = KS / kWaves, BLOCK = L::BLOCK;
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
         const int j = W * JW + jj;
         Op8 chi, clo, sg;
-        key_operands<LAYOUT, BITS, NI, NS>(c, j, tab_hi, tab_lo, chi, clo, sg);
-        uint8_t* base = buf + (j * 3) * BLOCK + lane * 16;
+        key_operands<LAYOUT, BITS, NI, NS, QJL>(c, j, tab_hi, tab_lo, chi, clo, sg);
+        uint8_t* base = buf + (j * L::NB) * BLOCK + lane * 16;
         *reinterpret_cast<uint4*>(base + 0 * BLOCK) = *reinterpret_cast<const uint4*>(chi.u);
         *reinterpret_cast<uint4*>(base + 1 * BLOCK) = *reinterpret_cast<const uint4*>(clo.u);
-        *reinterpret_cast<uint4*>(base + 2 * BLOCK) = *reinterpret_cast<const uint4*>(sg.u);
+        if constexpr (QJL) *reinterpret_cast<uint4*>(base + 2 * BLOCK) = *reinterpret_cast<const uint4*>(sg.u);
     }
 }
 
-template <int LAYOUT, int BITS, int D>
+// QJL = false: MSE-only keys (no sign stream, no T, gamma = the key's norm).
+template <int LAYOUT, int BITS, int D, bool QJL = true>
 __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
     const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
     float* __restrict__ scores, int B, int S, float coef) {
     using F = Fmt<LAYOUT, BITS>;
-    using L = SharedLds<LAYOUT, BITS, D>;
+    using L = SharedLds<LAYOUT, BITS, D, QJL>;
     constexpr int HALF = D / 2;
     constexpr int KS = D / 16;
     constexpr int NI = F::template idx_dw<D>();
     constexpr int NS = F::template sign_dw<D>();
+    constexpr int QT = QJL ? KS : 1;            // T operands kept (none without QJL)
     static_assert(KS % kWaves == 0, "each wavefront unpacks the same number of k-steps");
 
     __shared__ __attribute__((aligned(16))) uint8_t kops[2 * L::BUF];
@@ -931,15 +935,19 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
 #pragma unroll
     for (int k = 0; k < HALF; k += 4) {
         const float4 va = *reinterpret_cast<const float4*>(A + roff + k);
-        const float4 vt = *reinterpret_cast<const float4*>(T + roff + k);
         a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
-        t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+        if constexpr (QJL) {
+            const float4 vt = *reinterpret_cast<const float4*>(T + roff + k);
+            t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
+        } else {
+            t[k] = t[k + 1] = t[k + 2] = t[k + 3] = 0.f;
+        }
     }
     TileCodes<NI, NS> c0, c1;
     asm volatile("" ::: "memory");
-    load_tile<LAYOUT, BITS, D>(c0, idx, sign, gamma, key0 + min(tile * kTileKeys + col, S - 1), g);
-    load_tile<LAYOUT, BITS, D>(c1, idx, sign, gamma,
-                               key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+    load_tile<LAYOUT, BITS, D, QJL>(c0, idx, sign, gamma, key0 + min(tile * kTileKeys + col, S - 1), g);
+    load_tile<LAYOUT, BITS, D, QJL>(c1, idx, sign, gamma,
+                                    key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
     asm volatile("" ::: "memory");
     float sc;
     uint32_t tab_hi[4], tab_lo[4];
@@ -956,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     const float sA = pow2_scale_for(ma);
     const float sT = pow2_scale_for(mt);
     if (g == 0) rowk[wave][col] = make_float2(1.f / (sA * sc), coef / sT);
-    Op8 ahi[KS], alo[KS], thi[KS], tlo[KS];
+    Op8 ahi[KS], alo[KS], thi[QT], tlo[QT];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
 #pragma unroll
@@ -965,19 +973,21 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
             const _Float16 ha = (_Float16)xa;
             ahi[j].h[e] = ha;
             alo[j].h[e] = (_Float16)(xa - (float)ha);
-            const float xt = t[qjl_dim<LAYOUT>(j, e)] * sT;
-            const _Float16 ht = (_Float16)xt;
-            thi[j].h[e] = ht;
-            tlo[j].h[e] = (_Float16)(xt - (float)ht);
+            if constexpr (QJL) {
+                const float xt = t[qjl_dim<LAYOUT>(j, e)] * sT;
+                const _Float16 ht = (_Float16)xt;
+                thi[j].h[e] = ht;
+                tlo[j].h[e] = (_Float16)(xt - (float)ht);
+            }
         }
     }
 
     auto decode = [&](const TileCodes<NI, NS>& c, uint8_t* buf) __attribute__((always_inline)) {
         switch (wave) {
-            case 0: decode_share<LAYOUT, BITS, D, 0>(c, tab_hi, tab_lo, buf, lane); break;
-            case 1: decode_share<LAYOUT, BITS, D, 1>(c, tab_hi, tab_lo, buf, lane); break;
-            case 2: decode_share<LAYOUT, BITS, D, 2>(c, tab_hi, tab_lo, buf, lane); break;
-            default: decode_share<LAYOUT, BITS, D, 3>(c, tab_hi, tab_lo, buf, lane); break;
+            case 0: decode_share<LAYOUT, BITS, D, 0, QJL>(c, tab_hi, tab_lo, buf, lane); break;
+            case 1: decode_share<LAYOUT, BITS, D, 1, QJL>(c, tab_hi, tab_lo, buf, lane); break;
+            case 2: decode_share<LAYOUT, BITS, D, 2, QJL>(c, tab_hi, tab_lo, buf, lane); break;
+            default: decode_share<LAYOUT, BITS, D, 3, QJL>(c, tab_hi, tab_lo, buf, lane); break;
         }
     };
     decode(c0, kops);
@@ -995,29 +1005,37 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
         __attribute__((always_inline)) {
         if (t + stride < ntiles) decode(cn, other);
         const float gam_next = cn.gam;
-        load_tile<LAYOUT, BITS, D>(cr, idx, sign, gamma,
-                                   key0 + min(min(t + 2 * stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+        load_tile<LAYOUT, BITS, D, QJL>(cr, idx, sign, gamma,
+                                        key0 + min(min(t + 2 * stride, ntiles - 1) * kTileKeys + col, S - 1), g);
         f32x16 accM, accR;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { accM[v] = 0.f; accR[v] = 0.f; }
         const uint8_t* my = buf + lane * 16;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
-            Op8 chi, clo, sg;
-            *reinterpret_cast<uint4*>(chi.u) = *reinterpret_cast<const uint4*>(my + (j * 3 + 0) * L::BLOCK);
-            *reinterpret_cast<uint4*>(clo.u) = *reinterpret_cast<const uint4*>(my + (j * 3 + 1) * L::BLOCK);
-            *reinterpret_cast<uint4*>(sg.u) = *reinterpret_cast<const uint4*>(my + (j * 3 + 2) * L::BLOCK);
+            Op8 chi, clo;
+            *reinterpret_cast<uint4*>(chi.u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 0) * L::BLOCK);
+            *reinterpret_cast<uint4*>(clo.u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 1) * L::BLOCK);
             accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, chi.h, accM, 0, 0, 0);
-            accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, sg.h, accR, 0, 0, 0);
-            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, chi.h, accM, 0, 0, 0);
-            accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[j].h, sg.h, accR, 0, 0, 0);
+            if constexpr (QJL) {
+                Op8 sg;
+                *reinterpret_cast<uint4*>(sg.u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 2) * L::BLOCK);
+                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, sg.h, accR, 0, 0, 0);
+                accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, chi.h, accM, 0, 0, 0);
+                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[j].h, sg.h, accR, 0, 0, 0);
+            } else {
+                accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, chi.h, accM, 0, 0, 0);
+            }
             accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, clo.h, accM, 0, 0, 0);
         }
         const uint32_t lo = lane_offset(t * kTileKeys + col, S, g);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const float2 k = rowk[wave][8 * (v >> 2) + 4 * g + (v & 3)];
-            store_score(out_r, lo + row_offset(v, S), fmaf(k.y * gam_cur, accR[v], accM[v] * k.x));
+            if constexpr (QJL)
+                store_score(out_r, lo + row_offset(v, S), fmaf(k.y * gam_cur, accR[v], accM[v] * k.x));
+            else
+                store_score(out_r, lo + row_offset(v, S), (k.x * gam_cur) * accM[v]);
         }
         gam_cur = gam_next;
         __syncthreads();
@@ -1706,7 +1724,7 @@ hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, con
 
 // Shared-decode launch: workgroup rows are groups of four 32-query tiles; two
 // workgroups per CU are resident (registers), so 512 workgroups fill the chip.
-template <int LAYOUT, int BITS, int D>
+template <int LAYOUT, int BITS, int D, bool QJL = true>
 hipError_t launch_shared_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                            float* scores, int P, int B, int S, hipStream_t stream) {
     const int groups_y = (B + 127) / 128;
@@ -1716,17 +1734,17 @@ hipError_t launch_shared_d(const float* A, const float* T, KeyStreams k, const f
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_shared_kernel<LAYOUT, BITS, D>), dim3((unsigned)gx, groups_y, P),
+    hipLaunchKernelGGL((score_shared_kernel<LAYOUT, BITS, D, QJL>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();
 }
 
-template <int LAYOUT, int BITS>
+template <int LAYOUT, int BITS, bool QJL = true>
 hipError_t launch_shared_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                                 int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
-    if (D == 64) return launch_shared_d<LAYOUT, BITS, 64>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (D == 128) return launch_shared_d<LAYOUT, BITS, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 64) return launch_shared_d<LAYOUT, BITS, 64, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 128) return launch_shared_d<LAYOUT, BITS, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
     return hipErrorInvalidValue;
 }
 
@@ -1932,11 +1950,18 @@ hipError_t launch_score_mse(const float* A, const uint8_t* idx, const void* norm
                             hipStream_t stream) {
     if (!score_mse_supported(layout, bits, C, D)) return hipErrorInvalidValue;
     const KeyStreams k{idx, nullptr, norm};
-    // one group of four queries over many keys: the 16x16 tiles (as for tq_score)
-    if (pick_variant(layout, bits, C, B, (int64_t)P * S, D) == kMfmaSmall) {
+    // as for tq_score: one group of four queries over many keys takes the 16x16
+    // tiles, four or more query tiles the shared decode
+    const int variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
+    if (variant == kMfmaSmall) {
         if (layout == 0) return launch_small_layout<0, 0, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
         if (bits == 2) return launch_small_layout<1, 2, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
         return launch_small_layout<1, 3, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+    }
+    if (variant == kMfmaShared) {
+        if (layout == 0) return launch_shared_layout<0, 0, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+        if (bits == 2) return launch_shared_layout<1, 2, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
+        return launch_shared_layout<1, 3, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
     }
     if (layout == 0) return launch_layout<0, 0, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);
     if (bits == 2) return launch_layout<1, 2, false>(A, nullptr, k, codebook, C, scores, P, B, S, D, stream);

@@ -69,6 +69,10 @@ CASES = [
     ("packed", 3, 8, 128, 4, 2, 4, 2000, True),
     ("packed", 3, 8, 256, 1, 1, 40, 65, True),
     ("packed", 3, 8, 64, 1, 1, 96, 31, False),
+    # more than 96 queries: the shared-decode form
+    ("packed", 3, 8, 128, 2, 1, 128, 1000, True),
+    ("unpacked", 0, 4, 128, 1, 1, 200, 333, False),
+    ("packed", 2, 4, 128, 3, 3, 97, 65, False),
 ]
 
 
