@@ -684,6 +684,259 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Outlier split on the matrix cores ("TurboQuant: Rotate-then-Quantize KV
+// Caches at 3 Bits", section 7: two MSE-only instances per head, the hot
+// channels with one bit more). This kernel takes the page's 2.5-bit setting at
+// D = 128: 32 hot channels at 3 bits (8 centroids) and 96 at 2 bits (4), both
+// packed LSB-first with fp16 norms; a key's score is
+// rho_hi M_hi + rho_lo M_lo with M = <A, c[idx]> per instance.
+//
+// The LDS-staged layout of score_mfma_kernel with two contractions in one
+// 128-coordinate operand: lane half g holds hot coordinates [16 g, 16 g + 16)
+// in k-steps 0-1 (k-step j, element e: coordinate 16 g + 8 j + e) and the other
+// instance's [48 g, 48 g + 48) in k-steps 2-7 (the 2-bit order of the other
+// kernels over those 48). So every k-step belongs to one instance for both lane
+// halves: k-steps 0-1 accumulate M_hi, 2-7 M_lo, three split-f16 products each
+// (24 MFMAs per 32 x 32 tile). A lane's hot codes are 6 bytes (16 3-bit fields,
+// two 24-bit groups, one per k-step); its other codes 12 bytes (48 2-bit fields).
+// ---------------------------------------------------------------------------
+constexpr int kSplitDHi = 32;
+constexpr int kSplitDLo = 96;
+
+struct SplitTileCodes {
+    uint32_t h0, h1;        // dwords holding this lane's hot fields (see split_hot_groups)
+    uint32_t lw[3];         // this lane's 48 2-bit fields
+    float rho_hi, rho_lo;
+};
+
+// Codes of key `key` for lane half g: hot row 12 bytes (the lane's 6 start at
+// byte 6 g, read as the dwords at 4 g and 4 g + 4), other row 24 bytes (the
+// lane's 12 at byte 12 g).
+__device__ __forceinline__ void load_split_tile(SplitTileCodes& c, const uint8_t* __restrict__ idx_hi,
+                                                const void* __restrict__ norm_hi, const uint8_t* __restrict__ idx_lo,
+                                                const void* __restrict__ norm_lo, int64_t key, int g) {
+    const uint32_t* hp = reinterpret_cast<const uint32_t*>(idx_hi + key * 12 + 4 * g);
+    c.h0 = hp[0];
+    c.h1 = hp[1];
+    const uint32_t* lp = reinterpret_cast<const uint32_t*>(idx_lo + key * 24 + 12 * g);
+    c.lw[0] = lp[0];
+    c.lw[1] = lp[1];
+    c.lw[2] = lp[2];
+    c.rho_hi = (float)reinterpret_cast<const _Float16*>(norm_hi)[key];
+    c.rho_lo = (float)reinterpret_cast<const _Float16*>(norm_lo)[key];
+}
+
+// The two 24-bit groups of the lane's hot fields (fields 8 j .. 8 j + 7 in
+// group j): lane half 0's 48 bits start at bit 0 of h0, lane half 1's at bit 16.
+__device__ __forceinline__ void split_hot_groups(const SplitTileCodes& c, int g, uint32_t& v0, uint32_t& v1) {
+    v0 = __builtin_amdgcn_alignbit(c.h1, c.h0, g ? 16u : 0u) & 0xFFFFFFu;
+    v1 = (g ? (c.h1 >> 8) : __builtin_amdgcn_alignbit(c.h1, c.h0, 24u)) & 0xFFFFFFu;
+}
+
+// Selector bytes of four consecutive 3-bit fields of v (fields 0-3 of v).
+__device__ __forceinline__ uint32_t sel3x4(uint32_t v) {
+    return (v & 7u) | ((v << 5) & 0x700u) | ((v << 10) & 0x70000u) | ((v << 15) & 0x7000000u);
+}
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
+    const float* __restrict__ A_hi, const float* __restrict__ A_lo,
+    const uint8_t* __restrict__ idx_hi, const void* __restrict__ norm_hi,
+    const uint8_t* __restrict__ idx_lo, const void* __restrict__ norm_lo,
+    const float* __restrict__ cb_hi, int C_hi, const float* __restrict__ cb_lo, int C_lo,
+    float* __restrict__ scores, int B, int S) {
+    constexpr int D = kSplitDHi + kSplitDLo;
+    constexpr int KS = D / 16;                 // 2 hot k-steps, then 6
+    constexpr int BLOCK = 64 * 16;
+    constexpr int OPS_BYTES = MT * KS * 2 * BLOCK;
+    constexpr int SEG = 16;                    // coordinates each prologue lane converts
+    constexpr int PER_ROW = D / SEG;           // 2 hot blocks, 6 others
+    constexpr int ROWS_PER_PASS = kThreads / PER_ROW;
+
+    __shared__ __attribute__((aligned(16))) uint8_t ops[OPS_BYTES];
+    __shared__ float2 rowk[MT * 32];           // per-row epilogue factors (hot, other)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = blockIdx.z;
+    const int b0 = blockIdx.y * MT * 32;
+    const int rows = min(MT * 32, B - b0);
+    const int col = lane & 31;
+    const int g = lane >> 5;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    const int64_t key0 = (int64_t)p * S;
+    int tile = blockIdx.x * kWaves + wave;
+    const int stride = gridDim.x * kWaves;
+
+    SplitTileCodes cur;
+    float sch = 1.f, scl = 1.f;
+    uint32_t th_hi[4], th_lo[4], tl_hi[4], tl_lo[4];
+
+    // ---- query operands: lane pl of a row converts hot block pl (pl < 2) or
+    //      block pl - 2 of the others, scaled per row and instance by a power of two
+    for (int r0 = 0; r0 < MT * 32; r0 += ROWS_PER_PASS) {
+        const int row = r0 + tid / PER_ROW;
+        const int pl = tid % PER_ROW;
+        const bool hot = pl < 2;
+        const int rowc = min(row, rows - 1);
+        const float* src = hot ? A_hi + ((int64_t)p * B + b0 + rowc) * kSplitDHi + SEG * pl
+                               : A_lo + ((int64_t)p * B + b0 + rowc) * kSplitDLo + SEG * (pl - 2);
+        float a[SEG];
+#pragma unroll
+        for (int k = 0; k < SEG; k += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(src + k);
+            a[k] = v.x; a[k + 1] = v.y; a[k + 2] = v.z; a[k + 3] = v.w;
+        }
+        if (r0 == 0) {
+            asm volatile("" ::: "memory");
+            const int s = min(min(tile, ntiles - 1) * kTileKeys + col, S - 1);
+            load_split_tile(cur, idx_hi, norm_hi, idx_lo, norm_lo, key0 + s, g);
+            asm volatile("" ::: "memory");
+            codebook_tables(cb_hi, C_hi, sch, th_hi, th_lo);
+            codebook_tables(cb_lo, C_lo, scl, tl_hi, tl_lo);
+        }
+        if (row >= rows) {
+#pragma unroll
+            for (int k = 0; k < SEG; ++k) a[k] = 0.f;
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int k = 0; k < SEG; ++k) m = fmaxf(m, fabsf(a[k]));
+        float mh = hot ? m : 0.f, ml = hot ? 0.f : m;
+#pragma unroll
+        for (int o = 1; o < PER_ROW; o <<= 1) {
+            mh = fmaxf(mh, __shfl_xor(mh, o));
+            ml = fmaxf(ml, __shfl_xor(ml, o));
+        }
+        const float sh = pow2_scale_for(mh);
+        const float sl = pow2_scale_for(ml);
+        if (row < MT * 32 && pl == 0) rowk[row] = make_float2(1.f / (sh * sch), 1.f / (sl * scl));
+        if (row < MT * 32) {
+            const int mtile = row / 32, rl = row % 32;
+            const float sr = hot ? sh : sl;
+            int gg, blk16;
+            if (hot) {
+                gg = pl;                                  // hot coordinates 16 pl .. 16 pl + 15
+                blk16 = 0;
+            } else {
+                const int d0 = SEG * (pl - 2);            // other coordinates d0 .. d0 + 15
+                gg = d0 / (kSplitDLo / 2);
+                blk16 = (d0 % (kSplitDLo / 2)) / SEG;
+            }
+            uint8_t* lane_base = ops + (mtile * KS * 2) * BLOCK + (gg * 32 + rl) * 16;
+#pragma unroll
+            for (int k = 0; k < SEG; ++k) {
+                int j, e;
+                if (hot) {
+                    j = k / 8;
+                    e = k % 8;
+                } else {
+                    mse_slot16<1, 2>(blk16, k, j, e);
+                    j += 2;
+                }
+                uint16_t hi, lo;
+                split_f16(a[k] * sr, hi, lo);
+                uint8_t* base = lane_base + (j * 2) * BLOCK + e * 2;
+                *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = hi;
+                *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = lo;
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint8_t* my_ops = ops + lane * 16;
+
+    auto tile_scores = [&](const SplitTileCodes& c, int t) __attribute__((always_inline)) {
+        f32x16 accH[MT], accL[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { accH[mt][v] = 0.f; accL[mt][v] = 0.f; }
+        }
+        uint32_t hv[2];
+        split_hot_groups(c, g, hv[0], hv[1]);
+        // key-side operands of k-step j (hot table for j < 2)
+        auto key_ops = [&](int j, Op8& chi, Op8& clo) __attribute__((always_inline)) {
+            uint32_t x0, x1;
+            if (j < 2) {
+                x0 = sel3x4(hv[j]);
+                x1 = sel3x4(hv[j] >> 12);
+                lut4(x0, th_hi, chi.u[0], chi.u[1]);
+                lut4(x1, th_hi, chi.u[2], chi.u[3]);
+                lut4(x0, th_lo, clo.u[0], clo.u[1]);
+                lut4(x1, th_lo, clo.u[2], clo.u[3]);
+            } else {
+                Fmt<1, 2>::selectors<3>(c.lw, j - 2, x0, x1);
+                lut4(x0, tl_hi, chi.u[0], chi.u[1]);
+                lut4(x1, tl_hi, chi.u[2], chi.u[3]);
+                lut4(x0, tl_lo, clo.u[0], clo.u[1]);
+                lut4(x1, tl_lo, clo.u[2], clo.u[3]);
+            }
+        };
+        // as in score_mfma_kernel: k-step j + 1's key operands are built while
+        // k-step j's LDS reads and MFMAs are in flight
+        Op8 chi[2], clo[2];
+        key_ops(0, chi[0], clo[0]);
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int u = j & 1;
+            Op8 ahi[MT], alo[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t* base = my_ops + ((mt * KS + j) * 2) * BLOCK;
+                *reinterpret_cast<uint4*>(ahi[mt].u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
+                *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
+            }
+            if (j + 1 < KS) key_ops(j + 1, chi[u ^ 1], clo[u ^ 1]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x16& acc = j < 2 ? accH[mt] : accL[mt];
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, chi[u].h, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[mt].h, chi[u].h, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, clo[u].h, acc, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * MT, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+#pragma unroll
+            for (int i = 0; i < 3 * MT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, MT == 1 ? 5 : 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint32_t lo = lane_offset(t * kTileKeys + col, S, g);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const __amdgpu_buffer_rsrc_t out_r =
+                score_rows(scores + ((int64_t)p * B + b0 + mt * 32) * S, max(0, min(32, rows - mt * 32)), S);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float2 k = rowk[mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3)];
+                store_score(out_r, lo + row_offset(v, S),
+                            fmaf(k.y * c.rho_lo, accL[mt][v], (k.x * c.rho_hi) * accH[mt][v]));
+            }
+        }
+    };
+
+    if (tile < ntiles) {
+        SplitTileCodes nxt;
+        while (true) {
+            load_split_tile(nxt, idx_hi, norm_hi, idx_lo, norm_lo,
+                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+            tile_scores(cur, tile);
+            tile += stride;
+            if (tile >= ntiles) break;
+            load_split_tile(cur, idx_hi, norm_hi, idx_lo, norm_lo,
+                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+            tile_scores(nxt, tile);
+            tile += stride;
+            if (tile >= ntiles) break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Query-stationary variant: each wavefront keeps one 32-query tile's operands
 // (A_hi, A_lo, T_hi, T_lo: 4 x D/16 x 16 bytes per lane) in registers for its
 // whole life and streams key tiles past them, so the main loop touches LDS only
@@ -1887,6 +2140,38 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
 }
 
 bool score_mse_supported(int layout, int bits, int C, int D) { return lds_supported(layout, bits, C, D); }
+
+bool split_mfma_supported(int bits_hi, int C_hi, int bits_lo, int C_lo, int D_hi, int D_lo, int S) {
+    return bits_hi == 3 && C_hi == 8 && bits_lo == 2 && C_lo == 4 && D_hi == kSplitDHi && D_lo == kSplitDLo &&
+           S < (1 << 24);
+}
+
+namespace {
+template <int MT>
+hipError_t launch_split_mt(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
+                           const float* cb_lo, int C_lo, float* scores, int P, int B, int S, hipStream_t stream) {
+    // the grid of launch_mt: at most two workgroups per CU
+    const int groups_y = (B + MT * 32 - 1) / (MT * 32);
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    int64_t gx = (ntiles + kWaves - 1) / kWaves;
+    int64_t cap = 512 / ((int64_t)groups_y * P);
+    if (cap < 1) cap = 1;
+    if (gx > cap) gx = cap;
+    hipLaunchKernelGGL((score_split_mfma_kernel<MT>), dim3((unsigned)gx, groups_y, P), dim3(kThreads), 0, stream,
+                       A_hi, A_lo, k.idx_hi, k.norm_hi, k.idx_lo, k.norm_lo, cb_hi, C_hi, cb_lo, C_lo, scores, B, S);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_score_split_mfma(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
+                                   const float* cb_lo, int C_lo, float* scores, int P, int B, int S,
+                                   hipStream_t stream) {
+    switch (mt_for(B, kSplitDHi + kSplitDLo)) {
+        case 4: return launch_split_mt<4>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, stream);
+        case 2: return launch_split_mt<2>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, stream);
+        default: return launch_split_mt<1>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, stream);
+    }
+}
 
 namespace {
 

@@ -182,6 +182,8 @@ hipError_t launch_query_transform_split(const float* q, const int32_t* perm, con
 hipError_t launch_score_split(const float* A_hi, const float* A_lo, SplitStreams k, int bits_hi, int bits_lo,
                               const float* cb_hi, int C_hi, const float* cb_lo, int C_lo, float* scores, int P,
                               int B, int S, int D_hi, int D_lo, hipStream_t stream) {
+    if (split_mfma_supported(bits_hi, C_hi, bits_lo, C_lo, D_hi, D_lo, S))
+        return launch_score_split_mfma(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, stream);
     if (bits_hi == 0) return launch_split_lo<0>(bits_lo, A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
     if (bits_hi == 2) return launch_split_lo<2>(bits_lo, A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);
     return launch_split_lo<3>(bits_lo, A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, D_hi, D_lo, stream);

@@ -96,6 +96,12 @@ struct SplitStreams {
 hipError_t launch_query_transform_split(const float* q, const int32_t* perm, const float* Pi_hi, const float* Pi_lo,
                                         float* A_hi, float* A_lo, int P, int H, int B, int D, int D_hi,
                                         hipStream_t stream);
+// The 2.5-bit setting (32 hot channels packed at 3 bits, 96 at 2) on the
+// matrix cores; launch_score_split takes it when split_mfma_supported.
+bool split_mfma_supported(int bits_hi, int C_hi, int bits_lo, int C_lo, int D_hi, int D_lo, int S);
+hipError_t launch_score_split_mfma(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
+                                   const float* cb_lo, int C_lo, float* scores, int P, int B, int S,
+                                   hipStream_t stream);
 // bits_hi, bits_lo: 0 for one byte per index, else 2 or 3 (packed)
 hipError_t launch_score_split(const float* A_hi, const float* A_lo, SplitStreams k, int bits_hi, int bits_lo,
                               const float* cb_hi, int C_hi, const float* cb_lo, int C_lo, float* scores, int P,

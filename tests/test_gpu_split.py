@@ -88,6 +88,27 @@ def test_score_split_matches_oracle(hi_fmt, lo_fmt, D, d_hi, P, H, B, S):
     assert rel_err(got, ref) <= SCORE_TOL
 
 
+@pytest.mark.parametrize("P,H,B,S", [(1, 1, 64, 1000), (2, 1, 130, 333), (1, 1, 256, 4099), (3, 3, 33, 70000)])
+def test_score_split_matrix_core_shapes(P, H, B, S):
+    """The 2.5-bit setting (32 channels at 3 bits, 96 at 2, packed; the
+    matrix-core form) with one, two and four 32-query tiles per workgroup,
+    ragged query and key counts."""
+    say(f"score_split 2.5-bit P={P} B={B} S={S}")
+    rng = np.random.default_rng([P, B, S])
+    ih = rng.integers(0, 8, size=(P, S, 32), dtype=np.uint8)
+    il = rng.integers(0, 4, size=(P, S, 96), dtype=np.uint8)
+    gh, rh = instance_to_gpu(ih, rng.uniform(0.05, 1.5, (P, S)), "packed", 3)
+    gl, rl = instance_to_gpu(il, rng.uniform(0.3, 2.0, (P, S)), "packed", 2)
+    cb_hi, cb_lo = codebook_fp32(32, 8), codebook_fp32(96, 4)
+    A_hi = (rng.standard_normal((P, B, 32)) * 4.0).astype(np.float32)
+    A_lo = rng.standard_normal((P, B, 96)).astype(np.float32)
+    got = tq.tq_score_split(t(A_hi), t(A_lo), tq.SplitKeys(gh, gl), t(cb_hi), t(cb_lo)).cpu().numpy()
+    ref = np.stack([osp.scores_split_from_transformed(A_hi[p].astype(np.float64), ih[p], rh[p], cb_hi,
+                                                      A_lo[p].astype(np.float64), il[p], rl[p], cb_lo)
+                    for p in range(P)])
+    assert rel_err(got, ref) <= SCORE_TOL
+
+
 @pytest.mark.parametrize("nc", [False, True])
 def test_split_end_to_end_equals_reconstruction(nc):
     say(f"split transform then score, nc={nc}")
