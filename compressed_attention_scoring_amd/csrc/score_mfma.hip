@@ -1501,6 +1501,161 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
 constexpr int kMaxLdsBytes = 128 * 1024;
 
 // ---------------------------------------------------------------------------
+// Outlier split, four queries (B <= 4 over many keys): v_mfma_f32_16x16x32_f16
+// with the 16 keys of a tile as columns and, as rows, four queries times four
+// operand types: row 4 b + type holds, for query b, the hot instance's A_hi
+// (type 0) or A_lo (1) part, or the other instance's A_hi (2) or A_lo (3)
+// part, each zero outside its instance's coordinates. Lane group gq = lane / 16
+// owns 32 coordinates of its key: group 0 the 32 hot ones (3-bit, the key's
+// whole 12-byte row, the 3-bit order of the other kernels), groups 1-3 the
+// other instance's 32 (gq - 1) .. 32 gq - 1 (2-bit, 8 bytes, the 2-bit order),
+// each against its own instance's codebook. Two MFMAs per k-step: the
+// codebook's hi parts, then its lo parts, against the same rows (the lo rows
+// then add the A_lo c_lo term too). Lane 16 b + key ends with the four types of
+// (query b, key): rho_hi (t0 + t1) and rho_lo (t2 + t3) scaled back.
+// ---------------------------------------------------------------------------
+template <int MINW>
+__global__ __launch_bounds__(kThreads, MINW) void score_split16_kernel(
+    const float* __restrict__ A_hi, const float* __restrict__ A_lo,
+    const uint8_t* __restrict__ idx_hi, const void* __restrict__ norm_hi,
+    const uint8_t* __restrict__ idx_lo, const void* __restrict__ norm_lo,
+    const float* __restrict__ cb_hi, int C_hi, const float* __restrict__ cb_lo, int C_lo,
+    float* __restrict__ scores, int B, int S) {
+    constexpr int Q = 32;                          // coordinates per lane
+    constexpr int NJ = Q / 8;                      // k-steps
+    struct Codes {
+        uint32_t w[3];                             // hot row (group 0) or 8 bytes of the other row
+        float rho_hi, rho_lo;
+    };
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.z;
+    const int b0 = blockIdx.y * 4;
+    const int nb = min(4, B - b0);
+    const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
+    int tile = blockIdx.x * kWaves + wave;
+    const int stride = gridDim.x * kWaves;
+    if (tile >= ntiles) return;                    // no barrier in this kernel
+    const int gq = lane >> 4;
+    const int kc = lane & 15;
+    const int r = lane & 15;
+    const int rb = r >> 2, rtype = r & 3;
+    const bool hot = gq == 0;
+    const int64_t key0 = (int64_t)p * S;
+
+    // Branch-free: every lane reads three dwords; in groups 1-3 the third read
+    // repeats the first address (in bounds, unused).
+    auto load = [&](Codes& c, int64_t key) __attribute__((always_inline)) {
+        const uint32_t* a01 = reinterpret_cast<const uint32_t*>(hot ? idx_hi + key * 12
+                                                                    : idx_lo + key * 24 + 8 * (gq - 1));
+        const uint32_t* a2 = hot ? a01 + 2 : a01;
+        c.w[0] = a01[0];
+        c.w[1] = a01[1];
+        c.w[2] = a2[0];
+        c.rho_hi = (float)reinterpret_cast<const _Float16*>(norm_hi)[key];
+        c.rho_lo = (float)reinterpret_cast<const _Float16*>(norm_lo)[key];
+    };
+
+    // this lane's 32 query coordinates (query rb, clamped: queries past B are
+    // computed but never stored)
+    const int qb = b0 + min(rb, nb - 1);
+    const float* src = hot ? A_hi + ((int64_t)p * B + qb) * kSplitDHi
+                           : A_lo + ((int64_t)p * B + qb) * kSplitDLo + Q * (gq - 1);
+    float x[Q];
+#pragma unroll
+    for (int k = 0; k < Q; k += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + k);
+        x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
+    }
+    Codes cur;
+    asm volatile("" ::: "memory");
+    load(cur, key0 + min(tile * kTileKeys16 + kc, S - 1));
+    asm volatile("" ::: "memory");
+    float sch, scl;
+    uint32_t th_hi[4], th_lo[4], tl_hi[4], tl_lo[4];
+    codebook_tables(cb_hi, C_hi, sch, th_hi, th_lo);
+    codebook_tables(cb_lo, C_lo, scl, tl_hi, tl_lo);
+    uint32_t tab_hi[4], tab_lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tab_hi[i] = hot ? th_hi[i] : tl_hi[i];
+        tab_lo[i] = hot ? th_lo[i] : tl_lo[i];
+    }
+
+    // per-query, per-instance scales: maxima over lane group 0 (hot) and groups 1-3
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) m = fmaxf(m, fabsf(x[k]));
+    float mh = hot ? m : 0.f, ml = hot ? 0.f : m;
+    mh = fmaxf(mh, __shfl_xor(mh, 16));
+    mh = fmaxf(mh, __shfl_xor(mh, 32));
+    ml = fmaxf(ml, __shfl_xor(ml, 16));
+    ml = fmaxf(ml, __shfl_xor(ml, 32));
+    const float sh = pow2_scale_for(mh);
+    const float sl = pow2_scale_for(ml);
+    const float s_own = hot ? sh : sl;
+    // epilogue factors of output query gq (held by every lane with r = 4 gq)
+    const float kh = 1.f / (__shfl(sh, 4 * gq) * sch);
+    const float kl = 1.f / (__shfl(sl, 4 * gq) * scl);
+
+    // row operands: types 0/1 carry the hot coordinates (group 0 only), 2/3 the others
+    const bool live_hi = hot && rtype < 2, live_lo = !hot && rtype >= 2;
+    const bool part_lo = (rtype & 1) != 0;
+    Op8 ops[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = (hot ? x[mse_dim<1, 3>(j, e)] : x[mse_dim<1, 2>(j, e)]) * s_own;
+            const _Float16 h = (_Float16)xv;
+            const _Float16 l = (_Float16)(xv - (float)h);
+            ops[j].h[e] = (live_hi || live_lo) ? (part_lo ? l : h) : (_Float16)0.f;
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t out_r = score_rows(scores + ((int64_t)p * B + b0) * S, nb, S);
+
+    auto tile_scores = [&](const Codes& c, int t) __attribute__((always_inline)) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            uint32_t h0, h1, l0, l1;
+            Fmt<1, 3>::selectors<3>(c.w, j, h0, h1);
+            Fmt<1, 2>::selectors<3>(c.w, j, l0, l1);
+            const uint32_t x0 = hot ? h0 : l0, x1 = hot ? h1 : l1;
+            Op8 kh8, kl8;
+            lut4(x0, tab_hi, kh8.u[0], kh8.u[1]);
+            lut4(x1, tab_hi, kh8.u[2], kh8.u[3]);
+            lut4(x0, tab_lo, kl8.u[0], kl8.u[1]);
+            lut4(x1, tab_lo, kl8.u[2], kl8.u[3]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j].h, kh8.h, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j].h, kl8.h, acc, 0, 0, 0);
+        }
+        const int s = t * kTileKeys16 + kc;
+        const uint32_t off = s < S ? ((uint32_t)gq * (uint32_t)S + (uint32_t)s) * 4u : kDropKey;
+        store_score(out_r, off, fmaf(kl * c.rho_lo, acc[2] + acc[3], (kh * c.rho_hi) * (acc[0] + acc[1])));
+    };
+
+    // three code buffers in turn: each tile's codes are requested two tiles ahead
+    Codes nxt, nx2;
+    load(nxt, key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
+    while (true) {
+        load(nx2, key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
+        tile_scores(cur, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+        load(cur, key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
+        tile_scores(nxt, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+        load(nxt, key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
+        tile_scores(nx2, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fused decode step: scores, online softmax and value aggregation in one pass,
 // so no score reaches HBM ("Fitting 4.4x More Context on Jetson", section "v6:
 // Fused Vectorized Hybrid" and its online-softmax FAQ; "TurboQuant:
@@ -2166,6 +2321,19 @@ hipError_t launch_split_mt(const float* A_hi, const float* A_lo, SplitStreams k,
 hipError_t launch_score_split_mfma(const float* A_hi, const float* A_lo, SplitStreams k, const float* cb_hi, int C_hi,
                                    const float* cb_lo, int C_lo, float* scores, int P, int B, int S,
                                    hipStream_t stream) {
+    if (B <= 4 && (int64_t)P * S >= (int64_t(1) << 20)) {
+        // four queries over many keys: the 16x16 tiles (the rule tq_score uses);
+        // six wavefronts per SIMD fit its registers
+        constexpr int MINW = 6;
+        const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
+        int64_t gx = (ntiles + kWaves - 1) / kWaves;
+        int64_t cap = 256LL * MINW / P;
+        if (cap < 1) cap = 1;
+        if (gx > cap) gx = cap;
+        hipLaunchKernelGGL((score_split16_kernel<MINW>), dim3((unsigned)gx, 1, P), dim3(kThreads), 0, stream, A_hi,
+                           A_lo, k.idx_hi, k.norm_hi, k.idx_lo, k.norm_lo, cb_hi, C_hi, cb_lo, C_lo, scores, B, S);
+        return hipGetLastError();
+    }
     switch (mt_for(B, kSplitDHi + kSplitDLo)) {
         case 4: return launch_split_mt<4>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, stream);
         case 2: return launch_split_mt<2>(A_hi, A_lo, k, cb_hi, C_hi, cb_lo, C_lo, scores, P, B, S, stream);

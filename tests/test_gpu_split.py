@@ -88,11 +88,13 @@ def test_score_split_matches_oracle(hi_fmt, lo_fmt, D, d_hi, P, H, B, S):
     assert rel_err(got, ref) <= SCORE_TOL
 
 
-@pytest.mark.parametrize("P,H,B,S", [(1, 1, 64, 1000), (2, 1, 130, 333), (1, 1, 256, 4099), (3, 3, 33, 70000)])
+@pytest.mark.parametrize("P,H,B,S", [(1, 1, 64, 1000), (2, 1, 130, 333), (1, 1, 256, 4099), (3, 3, 33, 70000),
+                                     (16, 8, 4, 65537), (8, 1, 1, 131075), (32, 4, 3, 32769)])
 def test_score_split_matrix_core_shapes(P, H, B, S):
     """The 2.5-bit setting (32 channels at 3 bits, 96 at 2, packed; the
-    matrix-core form) with one, two and four 32-query tiles per workgroup,
-    ragged query and key counts."""
+    matrix-core forms) with one, two and four 32-query tiles per workgroup and,
+    for up to four queries over 2^20 keys or more, the 16x16 tiles; ragged
+    query and key counts."""
     say(f"score_split 2.5-bit P={P} B={B} S={S}")
     rng = np.random.default_rng([P, B, S])
     ih = rng.integers(0, 8, size=(P, S, 32), dtype=np.uint8)
