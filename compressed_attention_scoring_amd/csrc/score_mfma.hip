@@ -1479,16 +1479,27 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
             store_score(out_r, off, (kx * c.gam) * ((acc[0] + acc[1]) + acc[2]));
     };
 
-    TileCodes<NI, NS> nxt;
+    // three code buffers in turn: each tile's codes are requested two tiles ahead
+    TileCodes<NI, NS> nxt, nx2;
+    load_quarter<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
+                                       key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
     while (true) {
-        load_quarter<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
-                                           key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
+        load_quarter<LAYOUT, BITS, D, QJL>(nx2, idx, sign, gamma,
+                                           key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1),
+                                           gq);
         tile_scores(cur, tile);
         tile += stride;
         if (tile >= ntiles) break;
         load_quarter<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma,
-                                           key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
+                                           key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1),
+                                           gq);
         tile_scores(nxt, tile);
+        tile += stride;
+        if (tile >= ntiles) break;
+        load_quarter<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
+                                           key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1),
+                                           gq);
+        tile_scores(nx2, tile);
         tile += stride;
         if (tile >= ntiles) break;
     }
@@ -2103,12 +2114,13 @@ hipError_t launch_qs_d(const float* A, const float* T, KeyStreams k, const float
 }
 
 // Small-batch launch: workgroup rows are groups of four queries; MINW
-// wavefronts per SIMD are resident (the kernel needs about 100 registers at
-// D = 128), so 256 * MINW workgroups fill the chip.
+// wavefronts per SIMD are resident (the kernel needs about 105 registers at
+// D = 128 with signs), so 256 * MINW workgroups fill the chip.
 template <int LAYOUT, int BITS, int D, bool QJL = true>
 hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                           float* scores, int P, int B, int S, hipStream_t stream) {
-    constexpr int MINW = D <= 128 ? 4 : 2;
+    // without signs the kernel needs about 72 registers at D = 128: six wavefronts per SIMD
+    constexpr int MINW = D <= 128 ? (QJL ? 4 : 6) : 2;
     const int groups_y = (B + 3) / 4;
     const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
     int64_t gx = (ntiles + kWaves - 1) / kWaves;
