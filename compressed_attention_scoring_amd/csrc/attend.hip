@@ -399,18 +399,25 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
 
 // One workgroup per (query, problem): merge the chunks' (m, l, acc) and apply
 // Pi_v^T: out_j = sum_d Pi_v[d][j] a_d with a = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M).
-// Loads are issued in batches (NB chunk records per wavefront, all of a
-// thread's share of Pi_v) so each phase costs about one memory round trip.
+// The kernel is a chain of memory round trips, so it is shaped for as few as
+// possible: the thread's share of Pi_v is requested first, then every
+// wavefront requests its chunk records (wavefront w takes chunks w, w + 16, ...,
+// NB of them per batch of loads, one batch for up to 16 NB chunks) and merges
+// them with a running maximum of its own; the sixteen wavefront results are
+// merged through LDS.
+constexpr int kCombineThreads = 1024;   // attend_combine_kernel's workgroup: sixteen wavefronts
+
 template <int D>
-__global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
-                                                             float* __restrict__ out, int H, int B, int nch) {
+__global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
+                                                              float* __restrict__ out, int H, int B, int nch) {
+    constexpr int NW = kCombineThreads / 64;   // wavefronts
     constexpr int DL = (D + 63) / 64;      // coordinates per lane
-    constexpr int NB = 8;                  // chunk records per wavefront per batch of loads
-    constexpr int JP = 256 / D;            // threads per output coordinate in the product with Pi_v
+    constexpr int NB = 16;                 // chunk records per wavefront per batch of loads
+    constexpr int JP = NW * 64 / D;        // threads per output coordinate in the product with Pi_v
     constexpr int DJ = D / JP;             // coordinates each of them sums
-    __shared__ float part_a[4][D];
-    __shared__ float part_l[4];
-    __shared__ float wmax[4];
+    __shared__ float part_a[NW][D];
+    __shared__ float part_l[NW];
+    __shared__ float part_m[NW];
     __shared__ float a[D];
     __shared__ float po[JP][D];
     const int tid = threadIdx.x;
@@ -420,55 +427,70 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
     const int p = blockIdx.y;
     const float* rec = ws + ((int64_t)p * B + b) * nch * (D + 2);
 
-    float m = -INFINITY;
-    for (int c = tid; c < nch; c += 256) m = fmaxf(m, rec[(int64_t)c * (D + 2)]);
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) m = xor_max(m, s);
-    if (lane == 0) wmax[wave] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-
-    float acc[DL];
-#pragma unroll
-    for (int k = 0; k < DL; ++k) acc[k] = 0.f;
-    float den = 0.f;
-    for (int c0 = wave; c0 < nch; c0 += 4 * NB) {
-        float mv[NB], lv[NB], av[NB][DL];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int c = min(c0 + 4 * j, nch - 1);
-            const float* r = rec + (int64_t)c * (D + 2);
-            mv[j] = r[0];
-            lv[j] = r[1];
-#pragma unroll
-            for (int k = 0; k < DL; ++k) av[j][k] = r[2 + min(lane + 64 * k, D - 1)];
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const float f = c0 + 4 * j < nch ? __expf(mv[j] - M) : 0.f;
-            den = fmaf(lv[j], f, den);
-#pragma unroll
-            for (int k = 0; k < DL; ++k) acc[k] = fmaf(av[j][k], f, acc[k]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < DL; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) part_a[wave][d] = acc[k];
-    }
-    if (lane == 0) part_l[wave] = den;
-    __syncthreads();
-    if (tid < D) {
-        const float l = part_l[0] + part_l[1] + part_l[2] + part_l[3];
-        a[tid] = (part_a[0][tid] + part_a[1][tid] + part_a[2][tid] + part_a[3][tid]) / l;
-    }
-    __syncthreads();
+    // this thread's share of Pi_v (column j, rows h DJ .. h DJ + DJ - 1)
     const int j = tid % D;
     const int h = tid / D;
     const float* P = Pi_v + (int64_t)(p % H) * D * D + (int64_t)h * DJ * D + j;
     float pv[DJ];
 #pragma unroll
     for (int d = 0; d < DJ; ++d) pv[d] = P[(int64_t)d * D];
+
+    float mw = -INFINITY, den = 0.f;
+    float acc[DL];
+#pragma unroll
+    for (int k = 0; k < DL; ++k) acc[k] = 0.f;
+    for (int c0 = wave; c0 < nch; c0 += NW * NB) {
+        float mv[NB], lv[NB], av[NB][DL];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = min(c0 + NW * i, nch - 1);
+            const float* r = rec + (int64_t)c * (D + 2);
+            mv[i] = r[0];
+            lv[i] = r[1];
+#pragma unroll
+            for (int k = 0; k < DL; ++k) av[i][k] = r[2 + min(lane + 64 * k, D - 1)];
+        }
+        float bm = mw;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (c0 + NW * i < nch) bm = fmaxf(bm, mv[i]);
+        const float f0 = mw == -INFINITY ? 0.f : __expf(mw - bm);   // rescale what was merged so far
+        den *= f0;
+#pragma unroll
+        for (int k = 0; k < DL; ++k) acc[k] *= f0;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const float f = (c0 + NW * i < nch && mv[i] != -INFINITY) ? __expf(mv[i] - bm) : 0.f;
+            den = fmaf(lv[i], f, den);
+#pragma unroll
+            for (int k = 0; k < DL; ++k) acc[k] = fmaf(av[i][k], f, acc[k]);
+        }
+        mw = bm;
+    }
+#pragma unroll
+    for (int k = 0; k < DL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) part_a[wave][d] = acc[k];
+    }
+    if (lane == 0) {
+        part_l[wave] = den;
+        part_m[wave] = mw;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, part_m[w]);
+        float l = 0.f, v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = part_m[w] == -INFINITY ? 0.f : __expf(part_m[w] - M);
+            l = fmaf(part_l[w], f, l);
+            v = fmaf(part_a[w][tid], f, v);
+        }
+        a[tid] = v / l;
+    }
+    __syncthreads();
     float o = 0.f;
 #pragma unroll
     for (int d = 0; d < DJ; ++d) o = fmaf(pv[d], a[h * DJ + d], o);
@@ -561,9 +583,7 @@ hipError_t launch_attend_d(const float* scores, ValueStreams v, const float* cod
                              ? launch_partial<LAYOUT, BITS, D, kWide>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream)
                              : launch_partial<LAYOUT, BITS, D, kNarrow>(pl, scores, v, codebook, C, scale, ws, P, B, S, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)B, P), dim3(256), 0, stream, ws, Pi_v, out, H, B,
-                       pl.nch);
-    return hipGetLastError();
+    return launch_attend_combine(ws, Pi_v, out, P, H, B, D, pl.nch, stream);
 }
 
 template <int LAYOUT, int BITS>
@@ -581,9 +601,9 @@ hipError_t launch_attend_layout(const float* scores, ValueStreams v, const float
 hipError_t launch_attend_combine(const float* ws, const float* Pi_v, float* out, int P, int H, int B, int D, int nch,
                                  hipStream_t stream) {
     if (D == 64)
-        hipLaunchKernelGGL((attend_combine_kernel<64>), dim3((unsigned)B, P), dim3(256), 0, stream, ws, Pi_v, out, H, B, nch);
+        hipLaunchKernelGGL((attend_combine_kernel<64>), dim3((unsigned)B, P), dim3(kCombineThreads), 0, stream, ws, Pi_v, out, H, B, nch);
     else if (D == 128)
-        hipLaunchKernelGGL((attend_combine_kernel<128>), dim3((unsigned)B, P), dim3(256), 0, stream, ws, Pi_v, out, H, B, nch);
+        hipLaunchKernelGGL((attend_combine_kernel<128>), dim3((unsigned)B, P), dim3(kCombineThreads), 0, stream, ws, Pi_v, out, H, B, nch);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
