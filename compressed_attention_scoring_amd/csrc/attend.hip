@@ -402,17 +402,18 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
 // The kernel is a chain of memory round trips, so it is shaped for as few as
 // possible: the thread's share of Pi_v is requested first, then every
 // wavefront requests its chunk records (wavefront w takes chunks w, w + 16, ...,
-// NB of them per batch of loads, one batch for up to 16 NB chunks) and merges
-// them with a running maximum of its own; the sixteen wavefront results are
-// merged through LDS.
-constexpr int kCombineThreads = 1024;   // attend_combine_kernel's workgroup: sixteen wavefronts
+// NB of them per batch of loads, one batch for up to NW NB chunks) and merges
+// them with a running maximum of its own; the wavefront results are merged
+// through LDS.
+constexpr int kCombineBatch = 16;   // chunk records per wavefront per batch of loads
 
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
-                                                              float* __restrict__ out, int H, int B, int nch) {
-    constexpr int NW = kCombineThreads / 64;   // wavefronts
+// NW wavefronts (4 or 16: launch_attend_combine takes sixteen only when there
+// are more chunk records than four wavefronts take in one batch).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attend_combine_kernel(const float* __restrict__ ws, const float* __restrict__ Pi_v,
+                                                                 float* __restrict__ out, int H, int B, int nch) {
     constexpr int DL = (D + 63) / 64;      // coordinates per lane
-    constexpr int NB = 16;                 // chunk records per wavefront per batch of loads
+    constexpr int NB = kCombineBatch;
     constexpr int JP = NW * 64 / D;        // threads per output coordinate in the product with Pi_v
     constexpr int DJ = D / JP;             // coordinates each of them sums
     __shared__ float part_a[NW][D];
@@ -596,19 +597,24 @@ hipError_t launch_attend_layout(const float* scores, ValueStreams v, const float
 
 }  // namespace
 
-// The unpacked layout reads the most bytes per key, so it has the shortest
-// chunks and the most of them: its count bounds every layout's.
 hipError_t launch_attend_combine(const float* ws, const float* Pi_v, float* out, int P, int H, int B, int D, int nch,
                                  hipStream_t stream) {
-    if (D == 64)
-        hipLaunchKernelGGL((attend_combine_kernel<64>), dim3((unsigned)B, P), dim3(kCombineThreads), 0, stream, ws, Pi_v, out, H, B, nch);
-    else if (D == 128)
-        hipLaunchKernelGGL((attend_combine_kernel<128>), dim3((unsigned)B, P), dim3(kCombineThreads), 0, stream, ws, Pi_v, out, H, B, nch);
-    else
+    const dim3 grid((unsigned)B, P);
+    const bool wide = nch > 4 * kCombineBatch;   // more records than four wavefronts take in one batch
+    if (D == 64) {
+        if (wide) hipLaunchKernelGGL((attend_combine_kernel<64, 16>), grid, dim3(1024), 0, stream, ws, Pi_v, out, H, B, nch);
+        else hipLaunchKernelGGL((attend_combine_kernel<64, 4>), grid, dim3(256), 0, stream, ws, Pi_v, out, H, B, nch);
+    } else if (D == 128) {
+        if (wide) hipLaunchKernelGGL((attend_combine_kernel<128, 16>), grid, dim3(1024), 0, stream, ws, Pi_v, out, H, B, nch);
+        else hipLaunchKernelGGL((attend_combine_kernel<128, 4>), grid, dim3(256), 0, stream, ws, Pi_v, out, H, B, nch);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
+// The unpacked layout reads the most bytes per key, so it has the shortest
+// chunks and the most of them: its count bounds every layout's.
 int attend_chunks(int P, int B, int S, int D) { return make_plan(P, B, S, D, 0, 0).nmax; }
 
 bool attend_supported(int layout, int bits, int C, int D) {
