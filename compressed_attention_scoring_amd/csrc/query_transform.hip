@@ -130,27 +130,39 @@ __global__ __launch_bounds__(256) void query_transform_kernel(
 // columns, so the output rows of A and T are written as contiguous 128-byte runs.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Query rows of a workgroup: problems that share a head use the same W, so a
+// group of PG of them (problems h + H j, j = j0 .. j0 + PG - 1, for head h)
+// forms one list of PG * B query rows, cut into 32-row tiles: a few queries per
+// problem (GQA) still fill the MFMA rows. Row k of group g is query k % B of
+// problem h + H (j0 + k / B), with h = g % H and j0 = (g / H) PG.
 template <int D>
 __global__ __launch_bounds__(256) void query_transform_mfma_kernel(
     const float* __restrict__ q, const float* __restrict__ Pi,
     const float* __restrict__ S_mat, float* __restrict__ A, float* __restrict__ T,
-    int H, int B) {
+    int H, int B, int PG) {
     constexpr int KL = D / 8;                     // coordinates per lane half per wavefront
     __shared__ float part[4][64][17];             // partial tiles, padded against bank conflicts
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r0 = blockIdx.x * 32;               // first row of W = [Pi; S_mat] (2D rows)
-    const int b0 = blockIdx.y * 32;
-    const int p = blockIdx.z;
-    const int h = p % H;
+    const int b0 = blockIdx.y * 32;               // first row of this tile in the group's list
+    const int grp = blockIdx.z;
+    const int h = grp % H;
+    const int64_t j0 = (int64_t)(grp / H) * PG;
+    const int nrows = PG * B;
     const int i = lane & 31, half = lane >> 5;
     const int k0 = wave * (D / 4) + half * KL;
+    // flat query index (problem * B + query) of list row k (one problem per group:
+    // problem grp, no division)
+    auto qrow = [&](int k) -> int64_t {
+        return PG == 1 ? (int64_t)grp * B + k : (h + (int64_t)H * (j0 + k / B)) * B + k % B;
+    };
 
     const int wr = r0 + i;                        // W row this lane feeds (always < 2D)
     const float* wsrc = wr < D ? Pi + ((int64_t)h * D + wr) * D : S_mat + ((int64_t)h * D + wr - D) * D;
     const int b = b0 + i;
-    const int bc = b < B ? b : B - 1;             // unconditional load; zeroed below when b >= B
-    const float* qsrc = q + ((int64_t)p * B + bc) * D;
+    const int bc = b < nrows ? b : nrows - 1;     // unconditional load; zeroed below when past the list
+    const float* qsrc = q + qrow(bc) * D;
     float wv[KL], qv[KL];
 #pragma unroll
     for (int k = 0; k < KL; k += 4) {
@@ -159,7 +171,7 @@ __global__ __launch_bounds__(256) void query_transform_mfma_kernel(
         wv[k] = x.x; wv[k + 1] = x.y; wv[k + 2] = x.z; wv[k + 3] = x.w;
         qv[k] = y.x; qv[k + 1] = y.y; qv[k + 2] = y.z; qv[k + 3] = y.w;
     }
-    if (b >= B) {
+    if (b >= nrows) {
 #pragma unroll
         for (int k = 0; k < KL; ++k) qv[k] = 0.f;
     }
@@ -185,7 +197,7 @@ __global__ __launch_bounds__(256) void query_transform_mfma_kernel(
         const float y = (part[0][l][v] + part[1][l][v]) + (part[2][l][v] + part[3][l][v]);
         const int row = 8 * (v >> 2) + row_base + (v & 3);
         const int bb = b0 + row;
-        if (bb < B) out[((int64_t)p * B + bb) * D + d] = y;
+        if (bb < nrows) out[qrow(bb) * D + d] = y;
     }
 }
 
@@ -265,16 +277,19 @@ hipError_t launch_query_transform(const float* q, const float* Pi, const float* 
                                   float* A, float* T, int P, int H, int B, int D,
                                   hipStream_t stream) {
     if (D % 32 == 0 && D <= 256) {
-        dim3 grid(2 * D / 32, (B + 31) / 32, P);
+        // all P / H problems of a head in one row list when the tile count fits the grid
+        const int64_t per_head = (int64_t)(P / H) * B;
+        const int PG = (per_head + 31) / 32 <= 65535 ? P / H : 1;
+        dim3 grid(2 * D / 32, (unsigned)(((int64_t)PG * B + 31) / 32), (unsigned)(P / PG));
         switch (D) {
-            case 32: hipLaunchKernelGGL(query_transform_mfma_kernel<32>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            case 64: hipLaunchKernelGGL(query_transform_mfma_kernel<64>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            case 96: hipLaunchKernelGGL(query_transform_mfma_kernel<96>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            case 128: hipLaunchKernelGGL(query_transform_mfma_kernel<128>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            case 160: hipLaunchKernelGGL(query_transform_mfma_kernel<160>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            case 192: hipLaunchKernelGGL(query_transform_mfma_kernel<192>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            case 224: hipLaunchKernelGGL(query_transform_mfma_kernel<224>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
-            default: hipLaunchKernelGGL(query_transform_mfma_kernel<256>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B); break;
+            case 32: hipLaunchKernelGGL(query_transform_mfma_kernel<32>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 64: hipLaunchKernelGGL(query_transform_mfma_kernel<64>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 96: hipLaunchKernelGGL(query_transform_mfma_kernel<96>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 128: hipLaunchKernelGGL(query_transform_mfma_kernel<128>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 160: hipLaunchKernelGGL(query_transform_mfma_kernel<160>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 192: hipLaunchKernelGGL(query_transform_mfma_kernel<192>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 224: hipLaunchKernelGGL(query_transform_mfma_kernel<224>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            default: hipLaunchKernelGGL(query_transform_mfma_kernel<256>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
         }
         return hipGetLastError();
     }

@@ -59,7 +59,9 @@ def test_worked_example(golden):
 
 @pytest.mark.parametrize("P,H,B,D", [(1, 1, 1, 2), (1, 1, 2, 32), (1, 1, 32, 128), (3, 3, 5, 64),
                                      (16, 8, 4, 128), (1, 1, 128, 128), (2, 1, 7, 256),
-                                     (1, 1, 3, 1000), (2, 2, 17, 33)])
+                                     (1, 1, 3, 1000), (2, 2, 17, 33),
+                                     # problems of one head share 32-row tiles (rows span problems)
+                                     (128, 8, 4, 128), (6, 2, 33, 64), (12, 3, 1, 96)])
 def test_query_transform_parity(P, H, B, D):
     say(f"query_transform P={P} H={H} B={B} D={D}")
     rng = np.random.default_rng(P * 1000 + D)
