@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "tq_common.hpp"
+#include "value_sel.hpp"
 
 namespace tq {
 namespace {
@@ -292,48 +293,16 @@ __global__ __launch_bounds__(kWaves * 64) void attend_partial_kernel(
         uint64_t vb[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vb[e] = ((two ? (uint64_t)r.vhi[e] << 32 : 0ull) | r.vlo[e]) >> vsh;
-        // Packed fields (W <= 32 bits per key): byte-transpose first. tb[gk][k] holds
-        // byte k of the bits of keys 4 gk .. 4 gk + 3 (one key per byte), so a tile's
-        // field at bit o = BW t is (tb >> o % 8) & mask for all four keys at once; a
-        // 3-bit field that crosses into byte k + 1 is read from 16-bit windows.
+        // packed fields (W <= 32 bits per key): selectors from byte-transposed bits
         constexpr bool BYTES = LAYOUT == 1 && W <= 32;
-        constexpr int NBY = BYTES ? (W + 7) / 8 : 1;
-        uint32_t tb[2][NBY];
-        if constexpr (BYTES) {
-#pragma unroll
-            for (int gk = 0; gk < 2; ++gk) {
-                const uint32_t v0 = (uint32_t)vb[4 * gk], v1 = (uint32_t)vb[4 * gk + 1];
-                const uint32_t v2 = (uint32_t)vb[4 * gk + 2], v3 = (uint32_t)vb[4 * gk + 3];
-#pragma unroll
-                for (int k = 0; k < NBY; ++k) {
-                    const uint32_t lo_sel = (uint32_t)k | (uint32_t)(4 + k) << 8 | 0x0C0C0000u;
-                    const uint32_t hi_sel = 0x00000C0Cu | (uint32_t)k << 16 | (uint32_t)(4 + k) << 24;
-                    tb[gk][k] = perm(v1, v0, lo_sel) | perm(v3, v2, hi_sel);
-                }
-            }
-        }
+        using VS = typename std::conditional<BYTES, ValueSelectors<BW, W>, NoValueSelectors>::type;
+        const VS vs(vb);
         // value operands per tile and the products
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             uint32_t sel0 = 0, sel1 = 0;
             if constexpr (BYTES) {
-                constexpr uint32_t m8 = ((1u << BW) - 1u) * 0x01010101u;
-                constexpr uint32_t m16 = ((1u << BW) - 1u) * 0x00010001u;
-                const int o = BW * t, k = o >> 3, sh = o & 7;
-                uint32_t sel[2];
-#pragma unroll
-                for (int gk = 0; gk < 2; ++gk) {
-                    if (sh + BW <= 8) {
-                        sel[gk] = (tb[gk][k] >> sh) & m8;
-                    } else {
-                        const uint32_t a = tb[gk][k], b = tb[gk][k + 1];
-                        const uint32_t x01 = (perm(b, a, 0x05010400u) >> sh) & m16;   // keys 0, 1
-                        const uint32_t x23 = (perm(b, a, 0x07030602u) >> sh) & m16;   // keys 2, 3
-                        sel[gk] = perm(x23, x01, 0x06040200u);
-                    }
-                }
-                sel0 = sel[0];
-                sel1 = sel[1];
+                vs.tile(t, sel0, sel1);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {

@@ -39,7 +39,10 @@
 // query-side operands are built in the same order), so each key layout uses the
 // order in which its bitstream unpacks with the fewest instructions; see
 // mse_dim and qjl_dim.
+#include <type_traits>
+
 #include "tq_common.hpp"
+#include "value_sel.hpp"
 
 namespace tq {
 namespace {
@@ -1951,13 +1954,21 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
                 const int v = 8 * st + e;
                 vb[e] = ((vtwo ? (uint64_t)vr.hi[v] << 32 : 0ull) | vr.lo[v]) >> vsh;
             }
+            // packed fields (VW <= 32 bits per key): selectors from byte-transposed bits
+            constexpr bool BYTES = VLAYOUT == 1 && VW <= 32;
+            using VS = typename std::conditional<BYTES, ValueSelectors<VBW, VW>, NoValueSelectors>::type;
+            const VS vs(vb);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 uint32_t sel0 = 0, sel1 = 0;
+                if constexpr (BYTES) {
+                    vs.tile(tt, sel0, sel1);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sel0 |= ((uint32_t)(vb[e] >> (VBW * tt)) & ((1u << VBW) - 1u)) << (8 * e);
-                    sel1 |= ((uint32_t)(vb[4 + e] >> (VBW * tt)) & ((1u << VBW) - 1u)) << (8 * e);
+                    for (int e = 0; e < 4; ++e) {
+                        sel0 |= ((uint32_t)(vb[e] >> (VBW * tt)) & ((1u << VBW) - 1u)) << (8 * e);
+                        sel1 |= ((uint32_t)(vb[4 + e] >> (VBW * tt)) & ((1u << VBW) - 1u)) << (8 * e);
+                    }
                 }
                 Op8 vhi, vlo;
                 lut4(sel0, vtab_hi, vhi.u[0], vhi.u[1]);
