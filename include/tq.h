@@ -402,8 +402,11 @@ int tq_query_transform_split(const float* q, const int32_t* perm, const float* P
  *   codebooks  float32 [C_hi], [C_lo]: unpacked C <= 256, packed C == 2^bits
  *   scores     float32 [P, B, S]   output
  *
- * D_hi and D_lo multiples of 8 in [8, TQ_MAX_D]. fp32 arithmetic (vector ALU):
- * within 1e-4 * (1 + |exact|) of the exact value.
+ * D_hi and D_lo multiples of 8 in [8, TQ_MAX_D]. The 2.5-bit setting of the
+ * section (D_hi = 32 packed at 3 bits with C_hi = 8, D_lo = 96 packed at 2 bits
+ * with C_lo = 4, S < 2^24) runs on the matrix cores (f16 hi/lo parts of fp32
+ * operands, fp32 accumulation); other formats in fp32 on the vector ALU. Either
+ * way within 1e-4 * (1 + |exact|) of the exact value.
  */
 int tq_score_split(const float* A_hi, const float* A_lo, const tq_split_codes* keys,
                    const float* codebook_hi, int C_hi, const float* codebook_lo, int C_lo,
