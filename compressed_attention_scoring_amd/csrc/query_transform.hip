@@ -10,7 +10,7 @@
 //
 // The product is tiny (4 P B D^2 flops) and latency-bound, so both variants are
 // shaped for few dependent memory rounds. D a multiple of 32 up to 256 runs on
-// the matrix cores (query_transform_mfma_kernel below). Other D use the vector
+// the matrix cores (query_transform_mfma16_kernel below). Other D use the vector
 // kernel: a 256-lane workgroup owns 16 rows of W and 32 queries of one problem;
 // its operands are requested in one round of loads into LDS per 256 columns,
 // then every lane forms two outputs from broadcast LDS reads with eight
@@ -120,52 +120,57 @@ __global__ __launch_bounds__(256) void query_transform_kernel(
     if (b0 + bq + 16 < B) out[((int64_t)p * B + b0 + bq + 16) * D + d] = y1;
 }
 
-// Matrix-core variant for D in {32, 64, ..., 256} (D % 32 == 0): one 32x32 tile
-// of Y (32 queries x 32 rows of W) per workgroup, contracted with fp32 MFMA
-// (v_mfma_f32_32x32x2_f32: fp32 operands, fp32 accumulation, so no operand
-// splitting is needed). The contraction over D is split across the 4 wavefronts
-// (D/4 coordinates each, D/8 per lane half); every lane loads its operands for
-// the whole contraction with 16-byte loads in one round, and the four partial
-// tiles are summed through LDS. Queries are the MFMA rows and W rows the
-// columns, so the output rows of A and T are written as contiguous 128-byte runs.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
+// Matrix-core variant for D a multiple of 32 up to 256: one 16x16 tile of Y
+// (16 queries x 16 rows of W) per workgroup, contracted with fp32 MFMA
+// (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation, so no operand
+// splitting is needed). The contraction over D is split across NW wavefronts
+// (D / NW coordinates each, KM = D / (4 NW) per lane group of 16 lanes); every
+// lane loads its operands for the whole contraction with 16-byte loads in one
+// round, and the NW partial tiles are summed through LDS. Lane l feeds query
+// row l % 16 and W row l % 16 with the KM consecutive coordinates
+// k0 + KM (l / 16) + m, and MFMA m contracts coordinate m of every lane group,
+// so both operands take the same order. Queries are the MFMA rows and W rows
+// the columns: each query's outputs are written as contiguous 64-byte runs.
+// Small tiles keep the chain short: at 32 queries and D = 128 the grid has 32
+// workgroups, each with 8 KiB of operands and 8 dependent MFMAs per wavefront.
+//
 // Query rows of a workgroup: problems that share a head use the same W, so a
 // group of PG of them (problems h + H j, j = j0 .. j0 + PG - 1, for head h)
-// forms one list of PG * B query rows, cut into 32-row tiles: a few queries per
+// forms one list of PG * B query rows, cut into 16-row tiles: a few queries per
 // problem (GQA) still fill the MFMA rows. Row k of group g is query k % B of
 // problem h + H (j0 + k / B), with h = g % H and j0 = (g / H) PG.
-template <int D>
-__global__ __launch_bounds__(256) void query_transform_mfma_kernel(
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void query_transform_mfma16_kernel(
     const float* __restrict__ q, const float* __restrict__ Pi,
     const float* __restrict__ S_mat, float* __restrict__ A, float* __restrict__ T,
     int H, int B, int PG) {
-    constexpr int KL = D / 8;                     // coordinates per lane half per wavefront
-    __shared__ float part[4][64][17];             // partial tiles, padded against bank conflicts
+    constexpr int KM = D / (4 * NW);
+    static_assert(D % (16 * NW) == 0, "KM must be a whole number of float4s");
+    __shared__ float part[NW][64][5];             // partial tiles, padded against bank conflicts
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int r0 = blockIdx.x * 32;               // first row of W = [Pi; S_mat] (2D rows)
-    const int b0 = blockIdx.y * 32;               // first row of this tile in the group's list
+    const int r0 = blockIdx.x * 16;
+    const int b0 = blockIdx.y * 16;
     const int grp = blockIdx.z;
     const int h = grp % H;
     const int64_t j0 = (int64_t)(grp / H) * PG;
     const int nrows = PG * B;
-    const int i = lane & 31, half = lane >> 5;
-    const int k0 = wave * (D / 4) + half * KL;
-    // flat query index (problem * B + query) of list row k (one problem per group:
-    // problem grp, no division)
+    const int i = lane & 15, g = lane >> 4;
+    const int k0 = wave * (D / NW) + g * KM;
     auto qrow = [&](int k) -> int64_t {
         return PG == 1 ? (int64_t)grp * B + k : (h + (int64_t)H * (j0 + k / B)) * B + k % B;
     };
 
-    const int wr = r0 + i;                        // W row this lane feeds (always < 2D)
+    const int wr = r0 + i;                        // always < 2D: the grid has 2D / 16 column tiles
     const float* wsrc = wr < D ? Pi + ((int64_t)h * D + wr) * D : S_mat + ((int64_t)h * D + wr - D) * D;
     const int b = b0 + i;
-    const int bc = b < nrows ? b : nrows - 1;     // unconditional load; zeroed below when past the list
+    const int bc = b < nrows ? b : nrows - 1;
     const float* qsrc = q + qrow(bc) * D;
-    float wv[KL], qv[KL];
+    float wv[KM], qv[KM];
 #pragma unroll
-    for (int k = 0; k < KL; k += 4) {
+    for (int k = 0; k < KM; k += 4) {
         const float4 x = *reinterpret_cast<const float4*>(wsrc + k0 + k);
         const float4 y = *reinterpret_cast<const float4*>(qsrc + k0 + k);
         wv[k] = x.x; wv[k + 1] = x.y; wv[k + 2] = x.z; wv[k + 3] = x.w;
@@ -173,30 +178,25 @@ __global__ __launch_bounds__(256) void query_transform_mfma_kernel(
     }
     if (b >= nrows) {
 #pragma unroll
-        for (int k = 0; k < KL; ++k) qv[k] = 0.f;
+        for (int k = 0; k < KM; ++k) qv[k] = 0.f;
     }
-    f32x16 acc;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int k = 0; k < KM; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[k], wv[k], acc, 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < KL; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[k], wv[k], acc, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) part[wave][lane][v] = acc[v];
+    for (int v = 0; v < 4; ++v) part[wave][lane][v] = acc[v];
     __syncthreads();
-
-    // thread -> (lane of the tile layout, 4 of its 16 accumulator slots)
-    const int l = tid & 63, vg = tid >> 6;
-    const int col = l & 31;
-    const int row_base = 4 * (l >> 5);
-    const int wcol = r0 + col;
+    // element e of the tile -> (lane l of the tile layout, accumulator slot v): row 4 (l / 16) + v, column l % 16
+    const int l = tid & 63;
+    const int wcol = r0 + (l & 15);
     float* out = wcol < D ? A : T;
     const int d = wcol < D ? wcol : wcol - D;
+    for (int e = tid; e < 256; e += 64 * NW) {
+        const int v = e >> 6;
+        float y = part[0][l][v];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int v = 4 * vg + u;
-        const float y = (part[0][l][v] + part[1][l][v]) + (part[2][l][v] + part[3][l][v]);
-        const int row = 8 * (v >> 2) + row_base + (v & 3);
-        const int bb = b0 + row;
+        for (int w = 1; w < NW; ++w) y += part[w][l][v];
+        const int bb = b0 + 4 * (l >> 4) + v;
         if (bb < nrows) out[qrow(bb) * D + d] = y;
     }
 }
@@ -279,17 +279,27 @@ hipError_t launch_query_transform(const float* q, const float* Pi, const float* 
     if (D % 32 == 0 && D <= 256) {
         // all P / H problems of a head in one row list when the tile count fits the grid
         const int64_t per_head = (int64_t)(P / H) * B;
-        const int PG = (per_head + 31) / 32 <= 65535 ? P / H : 1;
-        dim3 grid(2 * D / 32, (unsigned)(((int64_t)PG * B + 31) / 32), (unsigned)(P / PG));
+        const int PG = (per_head + 15) / 16 <= 65535 ? P / H : 1;
+        dim3 grid(2 * D / 16, (unsigned)(((int64_t)PG * B + 15) / 16), (unsigned)(P / PG));
+        // four wavefronts split the contraction where D / 4 is a whole number of
+        // 16-coordinate steps, else two
         switch (D) {
-            case 32: hipLaunchKernelGGL(query_transform_mfma_kernel<32>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            case 64: hipLaunchKernelGGL(query_transform_mfma_kernel<64>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            case 96: hipLaunchKernelGGL(query_transform_mfma_kernel<96>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            case 128: hipLaunchKernelGGL(query_transform_mfma_kernel<128>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            case 160: hipLaunchKernelGGL(query_transform_mfma_kernel<160>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            case 192: hipLaunchKernelGGL(query_transform_mfma_kernel<192>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            case 224: hipLaunchKernelGGL(query_transform_mfma_kernel<224>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
-            default: hipLaunchKernelGGL(query_transform_mfma_kernel<256>, grid, dim3(256), 0, stream, q, Pi, S_mat, A, T, H, B, PG); break;
+            case 32: hipLaunchKernelGGL((query_transform_mfma16_kernel<32, 2>), grid, dim3(128), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            case 64: hipLaunchKernelGGL((query_transform_mfma16_kernel<64, 4>), grid, dim3(256), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            case 96: hipLaunchKernelGGL((query_transform_mfma16_kernel<96, 2>), grid, dim3(128), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            case 128: hipLaunchKernelGGL((query_transform_mfma16_kernel<128, 4>), grid, dim3(256), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            case 160: hipLaunchKernelGGL((query_transform_mfma16_kernel<160, 2>), grid, dim3(128), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            case 192: hipLaunchKernelGGL((query_transform_mfma16_kernel<192, 4>), grid, dim3(256), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            case 224: hipLaunchKernelGGL((query_transform_mfma16_kernel<224, 2>), grid, dim3(128), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
+            default: hipLaunchKernelGGL((query_transform_mfma16_kernel<256, 4>), grid, dim3(256), 0, stream,
+                                   q, Pi, S_mat, A, T, H, B, PG); break;
         }
         return hipGetLastError();
     }

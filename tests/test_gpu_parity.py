@@ -61,7 +61,10 @@ def test_worked_example(golden):
                                      (16, 8, 4, 128), (1, 1, 128, 128), (2, 1, 7, 256),
                                      (1, 1, 3, 1000), (2, 2, 17, 33),
                                      # problems of one head share 32-row tiles (rows span problems)
-                                     (128, 8, 4, 128), (6, 2, 33, 64), (12, 3, 1, 96)])
+                                     (128, 8, 4, 128), (6, 2, 33, 64), (12, 3, 1, 96),
+                                     # every D of the matrix-core form; 16-row tiles cut across problems
+                                     (2, 2, 17, 160), (1, 1, 16, 192), (3, 1, 15, 224), (4, 2, 9, 32),
+                                     (5, 1, 3, 128)])
 def test_query_transform_parity(P, H, B, D):
     say(f"query_transform P={P} H={H} B={B} D={D}")
     rng = np.random.default_rng(P * 1000 + D)
