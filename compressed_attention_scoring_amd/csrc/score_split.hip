@@ -6,10 +6,12 @@
 //                 + norm_lo[s] sum_j A_lo[b,j] cb_lo[idx_lo[s,j]],
 // with A_hi = Pi_hi q[hot channels] and A_lo = Pi_lo q[other channels].
 //
-// split_query_kernel: one workgroup per query; the query's channels, permuted
-// so the hot ones come first, are staged in LDS and each output coordinate is
-// one thread's dot product with its row of the instance's rotation (the
-// instances are small and not powers of two, so a dense product).
+// split_query_mfma_kernel: the two rotations' products on the fp32 matrix
+// cores, 16x16 tiles, when both instance sizes are multiples of 16 (below).
+// split_query_kernel, the other sizes: one workgroup per query; the query's
+// channels, permuted so the hot ones come first, are staged in LDS and each
+// output coordinate is one thread's dot product with its row of the instance's
+// rotation (the instances are small and not powers of two, so a dense product).
 //
 // score_split_kernel: one key per lane and QB queries per pass, both instances
 // in the same pass so each score is written once. The query operands are the
@@ -48,6 +50,71 @@ __global__ __launch_bounds__(kThreads) void split_query_kernel(const float* __re
         for (int j = 0; j < n; ++j) acc = fmaf(row[j], x[j], acc);
         if (hi) A_hi[((int64_t)p * B + b) * D_hi + r] = acc;
         else A_lo[((int64_t)p * B + b) * D_lo + r] = acc;
+    }
+}
+
+// Matrix-core form of the same products, for instance sizes that are multiples
+// of 16 up to 256: one 16x16 output tile (16 query rows x 16 rows of one
+// instance's rotation) per workgroup on v_mfma_f32_16x16x4_f32 (fp32 operands
+// and accumulation). The instance's N coordinates are split over N / 16
+// wavefronts, four consecutive coordinates per lane group of 16 lanes: lane l
+// loads one 16-byte piece of rotation row l % 16, the matching four entries of
+// perm and the four query values they name, for query row l % 16; the partial
+// tiles are summed through LDS. Query rows are listed as in the plain
+// transform: the P / H problems of a head form one list of rows when its tile
+// count fits the grid (row k is query k % B of problem h + H (j0 + k / B)).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSplitMaxWaves = 16;                // instances up to 256 coordinates
+
+__global__ __launch_bounds__(64 * kSplitMaxWaves) void split_query_mfma_kernel(
+    const float* __restrict__ q, const int32_t* __restrict__ perm, const float* __restrict__ Pi_hi,
+    const float* __restrict__ Pi_lo, float* __restrict__ A_hi, float* __restrict__ A_lo, int H, int B, int D,
+    int D_hi, int PG) {
+    __shared__ float part[kSplitMaxWaves][64][5];    // partial tiles, padded against bank conflicts
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * 16;               // output coordinate over [0, D): the hot instance first
+    const bool hot = r0 < D_hi;
+    const int N = hot ? D_hi : D - D_hi;          // the instance's size
+    const int off = hot ? 0 : D_hi;               // its first entry of perm
+    const int rr0 = r0 - off;                     // first row of its rotation in this tile
+    const int nw = N / 16;                        // wavefronts with coordinates
+    const int b0 = blockIdx.y * 16;
+    const int grp = blockIdx.z;
+    const int h = grp % H;
+    const int64_t j0 = (int64_t)(grp / H) * PG;
+    const int nrows = PG * B;
+    const int i = lane & 15, g = lane >> 4;
+    auto qrow = [&](int k) -> int64_t {
+        return PG == 1 ? (int64_t)grp * B + k : (h + (int64_t)H * (j0 + k / B)) * B + k % B;
+    };
+    if (wave < nw) {
+        const int k0 = wave * 16 + g * 4;         // this lane's four coordinates of the instance
+        const float* rot = (hot ? Pi_hi : Pi_lo) + (int64_t)h * N * N;
+        const float4 w = *reinterpret_cast<const float4*>(rot + (int64_t)(rr0 + i) * N + k0);
+        const int4 c = *reinterpret_cast<const int4*>(perm + off + k0);
+        const int b = b0 + i;
+        const float* qr = q + qrow(b < nrows ? b : nrows - 1) * D;
+        float x0 = qr[c.x], x1 = qr[c.y], x2 = qr[c.z], x3 = qr[c.w];
+        if (b >= nrows) x0 = x1 = x2 = x3 = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x0, w.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, w.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, w.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x3, w.w, acc, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[wave][lane][v] = acc[v];
+    }
+    __syncthreads();
+    // element e of the tile: lane l = e % 64 of the MFMA layout, slot v = e / 64,
+    // query row 4 (l / 16) + v, rotation row rr0 + l % 16
+    float* out = hot ? A_hi : A_lo;
+    for (int e = tid; e < 256; e += blockDim.x) {
+        const int l = e & 63, v = e >> 6;
+        float y = part[0][l][v];
+        for (int u = 1; u < nw; ++u) y += part[u][l][v];
+        const int bb = b0 + 4 * (l >> 4) + v;
+        if (bb < nrows) out[qrow(bb) * N + rr0 + (l & 15)] = y;
     }
 }
 
@@ -174,6 +241,18 @@ hipError_t launch_split_lo(int bits_lo, const float* A_hi, const float* A_lo, Sp
 hipError_t launch_query_transform_split(const float* q, const int32_t* perm, const float* Pi_hi, const float* Pi_lo,
                                         float* A_hi, float* A_lo, int P, int H, int B, int D, int D_hi,
                                         hipStream_t stream) {
+    const int D_lo = D - D_hi;
+    if (D_hi % 16 == 0 && D_lo % 16 == 0 && D_hi <= 16 * kSplitMaxWaves && D_lo <= 16 * kSplitMaxWaves) {
+        const int64_t per_head = (int64_t)(P / H) * B;
+        const int PG = (per_head + 15) / 16 <= 65535 ? P / H : 1;
+        const int64_t tiles = ((int64_t)PG * B + 15) / 16;
+        if (tiles <= 65535) {
+            const int waves = (D_hi > D_lo ? D_hi : D_lo) / 16;
+            hipLaunchKernelGGL(split_query_mfma_kernel, dim3((unsigned)(D / 16), (unsigned)tiles, (unsigned)(P / PG)),
+                               dim3(64 * waves), 0, stream, q, perm, Pi_hi, Pi_lo, A_hi, A_lo, H, B, D, D_hi, PG);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL(split_query_kernel, dim3((unsigned)B, (unsigned)P), dim3(kThreads), (size_t)D * sizeof(float),
                        stream, q, perm, Pi_hi, Pi_lo, A_hi, A_lo, H, B, D, D_hi);
     return hipGetLastError();

@@ -24,3 +24,17 @@ def load_golden(name: str) -> dict:
 @pytest.fixture
 def golden():
     return load_golden
+
+
+def pytest_collection_modifyitems(config, items):
+    """Tests marked gpu are skipped, not failed, where no GPU is visible."""
+    gpu_items = [item for item in items if "gpu" in item.keywords]
+    if not gpu_items:
+        return
+    import torch
+
+    if torch.cuda.is_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in gpu_items:
+        item.add_marker(skip)

@@ -48,7 +48,13 @@ def split_case(seed, P, H, S, D, d_hi, hi_fmt, lo_fmt, nc=False):
 
 
 @pytest.mark.parametrize("P,H,B,D,d_hi", [(1, 1, 1, 128, 32), (2, 2, 9, 128, 32), (4, 2, 33, 64, 16),
-                                          (1, 1, 5, 256, 96)])
+                                          (1, 1, 5, 256, 96),
+                                          # matrix-core form: 16-row tiles across a head's problems,
+                                          # the largest instance (15 wavefronts), partial query tiles
+                                          (8, 2, 3, 128, 32), (1, 1, 4, 256, 16), (3, 3, 17, 96, 48),
+                                          (16, 8, 4, 128, 32),
+                                          # instance sizes that are not multiples of 16: the vector form
+                                          (1, 1, 3, 128, 20), (2, 1, 5, 40, 8)])
 def test_query_transform_split(P, H, B, D, d_hi):
     say(f"split transform P={P} H={H} B={B} D={D} d_hi={d_hi}")
     rng = np.random.default_rng(D + B)
