@@ -38,7 +38,8 @@ __all__ = [
     "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform_hadamard",
     "tq_score_mse", "tq_score_attend", "tq_score_attend_workspace_bytes", "SplitKeys", "tq_query_transform_split", "tq_score_split", "tq_query_transform", "tq_score", "tq_score_with_kernel",
     "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
-    "TQ_UNPACKED", "TQ_PACKED", "KERNELS",
+    "TQ_UNPACKED", "TQ_PACKED", "KERNELS", "TQ_OK", "TQ_ERR_ARG", "TQ_ERR_UNSUPPORTED", "TQ_ERR_ALIGN",
+    "TQ_ERR_LAUNCH",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +47,10 @@ _LIB_PATH = os.path.join(_PKG, "libtq.so")
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "tq.h")
 
 TQ_OK = 0
+TQ_ERR_ARG = -1
+TQ_ERR_UNSUPPORTED = -2
+TQ_ERR_ALIGN = -3
+TQ_ERR_LAUNCH = -4
 TQ_UNPACKED = 0
 TQ_PACKED = 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_lds": 3, "mfma_reg": 4, "mfma16": 5, "mfma_shared": 6}
