@@ -110,6 +110,8 @@ int tq_query_transform(const float* q, const float* Pi, const float* S_mat, floa
 const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int S, int D, int kernel) {
     if (layout != TQ_UNPACKED && layout != TQ_PACKED) return nullptr;
     if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D) return nullptr;
+    // the sizes tq_score_with_kernel refuses
+    if (P > 65535 || B > 262144 || !fits(P, B, S) || !fits(P, B, D) || !fits(P, S, D)) return nullptr;
     if (layout == TQ_PACKED && ((bits != 2 && bits != 3) || D % 8 || C != (1 << bits))) return nullptr;
     if (layout == TQ_UNPACKED && (C < 1 || C > 256)) return nullptr;
     const int b = layout == TQ_PACKED ? bits : 0;
@@ -177,6 +179,7 @@ int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat, con
 
 size_t tq_attend_workspace_bytes(int P, int B, int S, int D) {
     if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
+    if (!fits(P, B, S) || !fits(P, S, D)) return 0;   // sizes tq_attend refuses
     const int64_t n = (int64_t)P * B * tq::attend_chunks(P, B, S, D) * (D + 2) * (int64_t)sizeof(float);
     return (size_t)n;
 }
@@ -210,6 +213,7 @@ namespace {
 // two passes with the scores in the workspace. Measured (us per call, fused /
 // two passes): B=32 S=131072 31 / 41, B=128 S=262144 118 / 141, B=32 S=32768
 // 22.5 / 20.5, P=128 B=4 404 / 255.
+// Callers have checked S < 2^24, which keeps the plan's int arithmetic in range.
 bool fused_step(int P, int B, int S, int& chunk, int& nch) {
     tq::score_attend_plan(P, B, S, chunk, nch);
     return B > 8 && chunk >= 8 * 32;
@@ -220,6 +224,8 @@ int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
 
 size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D, int mode) {
     if (P <= 0 || B <= 0 || S <= 0 || D <= 0 || D > TQ_MAX_D || P > 65535 || B > 262144) return 0;
+    // sizes tq_score_attend_with_mode refuses
+    if (S >= kMfmaMaxKeys || !fits(P, B, S) || !fits(P, B, D) || !fits(P, S, D)) return 0;
     if (mode != TQ_ATTEND_AUTO && mode != TQ_ATTEND_FUSED && mode != TQ_ATTEND_TWO_PASS) return 0;
     int chunk = 0, nch = 0;
     const bool fused = fused_step(P, B, S, chunk, nch);

@@ -558,7 +558,7 @@ Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
     pl.nt = ntfull / pl.dblk;
     const int64_t per = (S + n - 1) / n;
     pl.chunk = (int)((per + unit - 1) / unit * unit);
-    pl.nch = (S + pl.chunk - 1) / pl.chunk;
+    pl.nch = (int)(((int64_t)S + pl.chunk - 1) / pl.chunk);
     pl.nmax = (int)n;
     return pl;
 }

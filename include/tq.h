@@ -157,7 +157,8 @@ int tq_score_with_kernel(const float* A, const float* T, const tq_keys* keys,
 
 /*
  * tq_score_kernel_name: name of the kernel tq_score_with_kernel would launch
- * for this shape and format, or NULL if unsupported. Host-only, no GPU work.
+ * for this shape and format, or NULL if unsupported (including sizes
+ * tq_score_with_kernel refuses). Host-only, no GPU work.
  * The returned string is static.
  */
 const char* tq_score_kernel_name(int layout, int bits, int C, int P, int B, int S, int D, int kernel);
@@ -237,7 +238,8 @@ typedef tq_mse_codes tq_values;
 
 /*
  * tq_attend_workspace_bytes: bytes of the workspace tq_attend needs for this
- * shape with either value layout (0 for an empty shape or invalid sizes).
+ * shape with either value layout (0 for an empty shape, invalid sizes or sizes
+ * tq_attend refuses).
  * Host-only. The size depends only on (P, B, S, D).
  */
 size_t tq_attend_workspace_bytes(int P, int B, int S, int D);
@@ -281,8 +283,8 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
 
 /*
  * tq_score_attend_workspace_bytes: workspace tq_score_attend_with_mode needs
- * for this shape and form (0 for an empty shape, invalid sizes or an unknown
- * form). Host-only.
+ * for this shape and form (0 for an empty shape, invalid sizes, sizes
+ * tq_score_attend_with_mode refuses or an unknown form). Host-only.
  */
 size_t tq_score_attend_workspace_bytes(int P, int B, int S, int D, int mode);
 
