@@ -214,6 +214,38 @@ def time_phased_graphs(w, ring, shared, kernel, steps):
     return elapsed, 1e3 * qt_ms / steps, 1e3 * sc_ms / steps
 
 
+def stream_probe(device, nbytes: int) -> dict:
+    """A same-size reference for what one launch can move on this GPU: a
+    device-to-device copy of nbytes / 2 bytes (so nbytes are read and written
+    in total, like one tq_score launch's algorithmic bytes), replayed back to
+    back from a captured graph over distinct buffer pairs (>= 512 MB in all, so
+    no copy finds its source in the caches), timed with HIP events."""
+    import torch
+
+    half = max(256, (nbytes // 2) // 256 * 256)
+    npairs = max(2, min(64, math.ceil(RING_BYTES / (2 * half))))
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=device), torch.empty(half, dtype=torch.uint8, device=device))
+             for _ in range(npairs)]
+    for src, _ in pairs:
+        src.fill_(1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for src, dst in pairs:
+            dst.copy_(src)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, 2000 // npairs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / (reps * npairs)
+    return {"kind": "device-to-device copy (torch copy_), graph-replayed over distinct buffers",
+            "bytes": 2 * half, "us": us, "GB_s": 2 * half / (us * 1e-6) / 1e9}
+
+
 def cpu_baseline(w, host, target_s):
     """The float64 oracle (explicit key reconstruction) on the host cores."""
     import numpy as np
@@ -1001,6 +1033,11 @@ def main() -> int:
                           "launches of back-to-back transforms and back-to-back scores"),
         "ring_sets": len(ring),
     }
+    probe = stream_probe(device, alg_bytes)
+    probe["tq_score_frac_of_probe"] = achieved / probe["GB_s"]
+    out["stream_probe"] = probe
+    log(f"stream probe: {probe['bytes'] / 1e6:.1f} MB copied in {probe['us']:.2f} us ({probe['GB_s']:.0f} GB/s); "
+        f"tq_score at {probe['tq_score_frac_of_probe']:.2f} of it")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
