@@ -174,6 +174,71 @@ static_assert(slot16_matches<0, 0, 16>() && slot16_matches<0, 0, 128>() && slot1
               slot16_matches<1, 2, 128>() && slot16_matches<1, 3, 32>() && slot16_matches<1, 3, 128>(),
               "block-split slots");
 
+// Whole-slot prologue stores. For the unpacked layout (both operands) and the
+// 2-bit layout's codebook operand, the 16 coordinates of prologue block blk16
+// fill exactly slots 2 blk16 and 2 blk16 + 1 (all 8 elements of each), at
+// elements that do not depend on blk16, so a thread writes each part as two
+// 16-byte stores instead of sixteen 2-byte ones (which hit one LDS bank
+// eight ways). block_src<...>(s, e) is the block coordinate at element e of
+// slot 2 blk16 + s.
+template <int LAYOUT, int BITS, bool MSE>
+__host__ __device__ constexpr void block_slot16(int blk16, int k, int& j, int& e) {
+    if constexpr (MSE) mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
+    else qjl_slot16<LAYOUT>(blk16, k, j, e);
+}
+
+template <int LAYOUT, int BITS, bool MSE>
+constexpr int block_src(int s, int e) {
+    for (int k = 0; k < 16; ++k) {
+        int j = 0, ee = 0;
+        block_slot16<LAYOUT, BITS, MSE>(0, k, j, ee);
+        if (j == s && ee == e) return k;
+    }
+    return -1;
+}
+
+template <int LAYOUT, int BITS, bool MSE>
+constexpr bool whole_block_slots() {
+    for (int blk = 0; blk < 8; ++blk) {
+        bool seen[2][8] = {};
+        for (int k = 0; k < 16; ++k) {
+            int j = 0, e = 0, j0 = 0, e0 = 0;
+            block_slot16<LAYOUT, BITS, MSE>(blk, k, j, e);
+            block_slot16<LAYOUT, BITS, MSE>(0, k, j0, e0);
+            if (j0 < 0 || j0 > 1 || j != 2 * blk + j0 || e != e0 || seen[j0][e]) return false;
+            seen[j0][e] = true;
+        }
+    }
+    return true;
+}
+static_assert(whole_block_slots<0, 0, true>() && whole_block_slots<0, 0, false>() &&
+              whole_block_slots<1, 2, true>(), "whole-slot prologue layouts");
+
+// The packed layouts' sign operand: block blk16 fills the even (blk16 even) or
+// odd elements of slots 4 (blk16 >> 1) + c, c = 0..3, with coordinate 4 c + i
+// at element 2 i + (blk16 & 1); blocks blk16 and blk16 ^ 1 sit in adjacent
+// lanes and complete each other's slots.
+constexpr bool packed_sign_pairs() {
+    for (int blk = 0; blk < 8; ++blk)
+        for (int k = 0; k < 16; ++k) {
+            int j = 0, e = 0;
+            qjl_slot16<1>(blk, k, j, e);
+            if (j != 4 * (blk >> 1) + k / 4 || e != 2 * (k % 4) + (blk & 1)) return false;
+        }
+    return true;
+}
+static_assert(packed_sign_pairs(), "packed sign slots");
+
+template <int LAYOUT, int BITS, bool MSE>
+__device__ __forceinline__ uint4 whole_slot(const uint16_t (&v)[16], int s) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        w[q] = (uint32_t)v[block_src<LAYOUT, BITS, MSE>(s, 2 * q)] |
+               ((uint32_t)v[block_src<LAYOUT, BITS, MSE>(s, 2 * q + 1)] << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Compile-time proof that every coordinate of a lane half lands in exactly one
 // (k-step, element) slot of each contraction and that the slot maps invert.
 template <int LAYOUT, int BITS, int HALF>
@@ -473,6 +538,103 @@ __device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template 
     else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
 }
 
+// Prologue stores of one 16-coordinate block of a query row (block blk16 of
+// lane segment lane_base) into the LDS operand blocks: parts 0/1 the A hi/lo
+// halves, 2/3 the T halves. Whole 16-byte slots where the layout allows
+// (whole_block_slots, packed_sign_pairs); the 3-bit codebook operand keeps
+// 2-byte stores. `live` is false for rows past the tile: such lanes still take
+// part in the sign exchange with their neighbour but store nothing.
+template <int LAYOUT, int BITS, bool QJL, int SEG>
+__device__ __forceinline__ void prologue_store(uint8_t* lane_base, int blk16, const float (&a)[SEG],
+                                               const float (&t)[SEG], float sA, float sT, bool live) {
+    static_assert(SEG == 16, "blocks of 16 coordinates");
+    constexpr int BLOCK = 64 * 16;
+    constexpr bool WHOLE_MSE = LAYOUT == 0 || BITS == 2;    // whole_block_slots holds
+    uint16_t ah[SEG], al[SEG];
+#pragma unroll
+    for (int k = 0; k < SEG; ++k) split_f16(a[k] * sA, ah[k], al[k]);
+    if constexpr (WHOLE_MSE) {
+        if (live) {
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                uint8_t* base = lane_base + ((2 * blk16 + sl) * 4) * BLOCK;
+                *reinterpret_cast<uint4*>(base + 0 * BLOCK) = whole_slot<LAYOUT, BITS, true>(ah, sl);
+                *reinterpret_cast<uint4*>(base + 1 * BLOCK) = whole_slot<LAYOUT, BITS, true>(al, sl);
+            }
+        }
+    } else if (live) {
+#pragma unroll
+        for (int k = 0; k < SEG; ++k) {
+            int j, e;
+            mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
+            uint8_t* base = lane_base + (j * 4) * BLOCK + e * 2;
+            *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = ah[k];
+            *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = al[k];
+        }
+    }
+    if constexpr (QJL) {
+        uint16_t th[SEG], tl[SEG];
+#pragma unroll
+        for (int k = 0; k < SEG; ++k) split_f16(t[k] * sT, th[k], tl[k]);
+        if constexpr (LAYOUT == 0) {
+            if (live) {
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    uint8_t* base = lane_base + ((2 * blk16 + sl) * 4) * BLOCK;
+                    *reinterpret_cast<uint4*>(base + 2 * BLOCK) = whole_slot<LAYOUT, BITS, false>(th, sl);
+                    *reinterpret_cast<uint4*>(base + 3 * BLOCK) = whole_slot<LAYOUT, BITS, false>(tl, sl);
+                }
+            }
+        } else {
+            // packed_sign_pairs: this lane (hb = blk16 & 1) and lane ^ 1 (the other
+            // parity, same row and segment) share slots 4 (blk16 >> 1) + c. The
+            // lane with hb writes slots c = 2 hb, 2 hb + 1 whole: it keeps its own
+            // coordinates 4 c + i of those slots and receives the partner's.
+            // Word w of slot c holds i = 2 w (low half) and 2 w + 1 (high half).
+            const bool odd = (blk16 & 1) != 0;
+            uint32_t own_h[4][2], own_l[4][2];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    own_h[c][w] = (uint32_t)th[4 * c + 2 * w] | ((uint32_t)th[4 * c + 2 * w + 1] << 16);
+                    own_l[c][w] = (uint32_t)tl[4 * c + 2 * w] | ((uint32_t)tl[4 * c + 2 * w + 1] << 16);
+                }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                uint32_t mine_h[2], mine_l[2], got_h[2], got_l[2];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    // send the partner's slots (2 (1 - hb) + cc), keep this lane's (2 hb + cc)
+                    const uint32_t send_h = odd ? own_h[cc][w] : own_h[2 + cc][w];
+                    const uint32_t send_l = odd ? own_l[cc][w] : own_l[2 + cc][w];
+                    mine_h[w] = odd ? own_h[2 + cc][w] : own_h[cc][w];
+                    mine_l[w] = odd ? own_l[2 + cc][w] : own_l[cc][w];
+                    got_h[w] = (uint32_t)__shfl_xor((int)send_h, 1);
+                    got_l[w] = (uint32_t)__shfl_xor((int)send_l, 1);
+                }
+                // element 2 i + parity: the even lane's value, then the odd lane's
+                uint32_t oh[4], ol[4];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const uint32_t e0h = odd ? got_h[w] : mine_h[w], e1h = odd ? mine_h[w] : got_h[w];
+                    const uint32_t e0l = odd ? got_l[w] : mine_l[w], e1l = odd ? mine_l[w] : got_l[w];
+                    oh[2 * w] = __builtin_amdgcn_perm(e1h, e0h, 0x05040100u);
+                    oh[2 * w + 1] = __builtin_amdgcn_perm(e1h, e0h, 0x07060302u);
+                    ol[2 * w] = __builtin_amdgcn_perm(e1l, e0l, 0x05040100u);
+                    ol[2 * w + 1] = __builtin_amdgcn_perm(e1l, e0l, 0x07060302u);
+                }
+                if (live) {
+                    const int j = 4 * (blk16 >> 1) + 2 * (blk16 & 1) + cc;
+                    uint8_t* base = lane_base + (j * 4) * BLOCK;
+                    *reinterpret_cast<uint4*>(base + 2 * BLOCK) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+                    *reinterpret_cast<uint4*>(base + 3 * BLOCK) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+                }
+            }
+        }
+    }
+}
+
 // QJL = false scores MSE-only keys: scores = norm_s * M (no T, no signs).
 template <int LAYOUT, int BITS, int D, int MT, bool QJL>
 __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
@@ -572,30 +734,12 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         const float sT = pow2_scale_for(mt);
         // sA, sT and sc are powers of two, so these factors are exact
         if (row < MT * 32 && pl == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
-        if (row < MT * 32) {
-            const int mtile = row / 32, rl = row % 32;
-            const int d0 = pl * SEG;
-            const int gg = d0 / HALF;                           // lane segment holding these coordinates
-            const int blk16 = (d0 % HALF) / SEG;                // their 16-coordinate block in it
-            uint8_t* lane_base = ops + (mtile * KS * 4) * BLOCK + (gg * 32 + rl) * 16;
-#pragma unroll
-            for (int k = 0; k < SEG; ++k) {
-                uint16_t hi, lo;
-                int j, e;
-                mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
-                split_f16(a[k] * sA, hi, lo);
-                uint8_t* base = lane_base + (j * 4) * BLOCK + e * 2;
-                *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = hi;
-                *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = lo;
-                if constexpr (QJL) {
-                    qjl_slot16<LAYOUT>(blk16, k, j, e);
-                    split_f16(t[k] * sT, hi, lo);
-                    base = lane_base + (j * 4) * BLOCK + e * 2;
-                    *reinterpret_cast<uint16_t*>(base + 2 * BLOCK) = hi;
-                    *reinterpret_cast<uint16_t*>(base + 3 * BLOCK) = lo;
-                }
-            }
-        }
+        const int mtile = row / 32, rl = row % 32;
+        const int d0 = pl * SEG;
+        const int gg = d0 / HALF;                               // lane segment holding these coordinates
+        const int blk16 = (d0 % HALF) / SEG;                    // their 16-coordinate block in it
+        uint8_t* lane_base = ops + (mtile * KS * 4) * BLOCK + (gg * 32 + rl) * 16;
+        prologue_store<LAYOUT, BITS, QJL, SEG>(lane_base, blk16, a, t, sA, sT, row < MT * 32);
     }
     __syncthreads();
 
@@ -1791,26 +1935,12 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
         const float sA = pow2_scale_for(ma);
         const float sT = pow2_scale_for(mt);
         if (row < 32 && pl == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
-        if (row < 32) {
+        {
             const int d0 = pl * SEG;
             const int gg = d0 / HALF;
             const int blk16 = (d0 % HALF) / SEG;
             uint8_t* lane_base = ops + (gg * 32 + row) * 16;
-#pragma unroll
-            for (int k = 0; k < SEG; ++k) {
-                uint16_t hi, lo;
-                int j, e;
-                mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
-                split_f16(a[k] * sA, hi, lo);
-                uint8_t* base = lane_base + (j * 4) * BLOCK + e * 2;
-                *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = hi;
-                *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = lo;
-                qjl_slot16<LAYOUT>(blk16, k, j, e);
-                split_f16(t[k] * sT, hi, lo);
-                base = lane_base + (j * 4) * BLOCK + e * 2;
-                *reinterpret_cast<uint16_t*>(base + 2 * BLOCK) = hi;
-                *reinterpret_cast<uint16_t*>(base + 3 * BLOCK) = lo;
-            }
+            prologue_store<LAYOUT, BITS, true, SEG>(lane_base, blk16, a, t, sA, sT, row < 32);
         }
     }
 
