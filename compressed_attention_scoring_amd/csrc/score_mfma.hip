@@ -538,14 +538,26 @@ __device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template 
     else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
 }
 
+// Position of operand lane p's 16-byte slot in the LDS block of k-step j. The
+// blocks of different k-steps sit 4 KiB apart (the same banks), so the eight
+// 16-coordinate blocks of a query row, written together in the prologue, would
+// all hit the same banks; XOR-ing bits 2-4 with the block (j >> 1) and bit 1
+// with the lane half (bit 5) spreads them, while the 16 lanes of every quarter
+// wave that read one k-step's block still cover 16 distinct slots (a bijection
+// that keeps bits 4-5 of p within each group of 16).
+__device__ __forceinline__ int slot_pos(int p, int j) {
+    return p ^ (((j >> 1) & 7) << 2) ^ (((p >> 5) & 1) << 1);
+}
+
 // Prologue stores of one 16-coordinate block of a query row (block blk16 of
-// lane segment lane_base) into the LDS operand blocks: parts 0/1 the A hi/lo
+// operand lane p: segment p / 32, row p % 32) into the LDS operand blocks of a
+// 32-query tile starting at tile_base: parts 0/1 the A hi/lo
 // halves, 2/3 the T halves. Whole 16-byte slots where the layout allows
 // (whole_block_slots, packed_sign_pairs); the 3-bit codebook operand keeps
 // 2-byte stores. `live` is false for rows past the tile: such lanes still take
 // part in the sign exchange with their neighbour but store nothing.
 template <int LAYOUT, int BITS, bool QJL, int SEG>
-__device__ __forceinline__ void prologue_store(uint8_t* lane_base, int blk16, const float (&a)[SEG],
+__device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int blk16, const float (&a)[SEG],
                                                const float (&t)[SEG], float sA, float sT, bool live) {
     static_assert(SEG == 16, "blocks of 16 coordinates");
     constexpr int BLOCK = 64 * 16;
@@ -557,7 +569,8 @@ __device__ __forceinline__ void prologue_store(uint8_t* lane_base, int blk16, co
         if (live) {
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
-                uint8_t* base = lane_base + ((2 * blk16 + sl) * 4) * BLOCK;
+                const int j = 2 * blk16 + sl;
+                uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16;
                 *reinterpret_cast<uint4*>(base + 0 * BLOCK) = whole_slot<LAYOUT, BITS, true>(ah, sl);
                 *reinterpret_cast<uint4*>(base + 1 * BLOCK) = whole_slot<LAYOUT, BITS, true>(al, sl);
             }
@@ -567,7 +580,7 @@ __device__ __forceinline__ void prologue_store(uint8_t* lane_base, int blk16, co
         for (int k = 0; k < SEG; ++k) {
             int j, e;
             mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
-            uint8_t* base = lane_base + (j * 4) * BLOCK + e * 2;
+            uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16 + e * 2;
             *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = ah[k];
             *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = al[k];
         }
@@ -580,7 +593,8 @@ __device__ __forceinline__ void prologue_store(uint8_t* lane_base, int blk16, co
             if (live) {
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl) {
-                    uint8_t* base = lane_base + ((2 * blk16 + sl) * 4) * BLOCK;
+                    const int j = 2 * blk16 + sl;
+                    uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16;
                     *reinterpret_cast<uint4*>(base + 2 * BLOCK) = whole_slot<LAYOUT, BITS, false>(th, sl);
                     *reinterpret_cast<uint4*>(base + 3 * BLOCK) = whole_slot<LAYOUT, BITS, false>(tl, sl);
                 }
@@ -626,7 +640,7 @@ __device__ __forceinline__ void prologue_store(uint8_t* lane_base, int blk16, co
                 }
                 if (live) {
                     const int j = 4 * (blk16 >> 1) + 2 * (blk16 & 1) + cc;
-                    uint8_t* base = lane_base + (j * 4) * BLOCK;
+                    uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16;
                     *reinterpret_cast<uint4*>(base + 2 * BLOCK) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
                     *reinterpret_cast<uint4*>(base + 3 * BLOCK) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
                 }
@@ -738,12 +752,11 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         const int d0 = pl * SEG;
         const int gg = d0 / HALF;                               // lane segment holding these coordinates
         const int blk16 = (d0 % HALF) / SEG;                    // their 16-coordinate block in it
-        uint8_t* lane_base = ops + (mtile * KS * 4) * BLOCK + (gg * 32 + rl) * 16;
-        prologue_store<LAYOUT, BITS, QJL, SEG>(lane_base, blk16, a, t, sA, sT, row < MT * 32);
+        prologue_store<LAYOUT, BITS, QJL, SEG>(ops + (mtile * KS * 4) * BLOCK, gg * 32 + rl, blk16, a, t, sA, sT,
+                                               row < MT * 32);
     }
     __syncthreads();
 
-    const uint8_t* my_ops = ops + lane * 16;
 
     // One tile: the key-side operands of k-step j + 1 are built while the LDS
     // reads and MFMAs of step j are in flight, then the scores are scaled and
@@ -766,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             Op8 ahi[MT], alo[MT], thi[MT], tlo[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* base = my_ops + ((mt * KS + j) * 4) * BLOCK;
+                const uint8_t* base = ops + ((mt * KS + j) * 4) * BLOCK + slot_pos(lane, j) * 16;
                 *reinterpret_cast<uint4*>(ahi[mt].u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
                 *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
                 if constexpr (QJL) {
@@ -1939,8 +1952,7 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
             const int d0 = pl * SEG;
             const int gg = d0 / HALF;
             const int blk16 = (d0 % HALF) / SEG;
-            uint8_t* lane_base = ops + (gg * 32 + row) * 16;
-            prologue_store<LAYOUT, BITS, true, SEG>(lane_base, blk16, a, t, sA, sT, row < 32);
+            prologue_store<LAYOUT, BITS, true, SEG>(ops, gg * 32 + row, blk16, a, t, sA, sT, row < 32);
         }
     }
 
@@ -1986,7 +1998,6 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
     float lsum = 0.f;          // sum of exp(scale*score - M) over this lane's keys
     float nexp = -1000.f;      // value norms are scaled by 2^-nexp ...
     float nlim = 0.f;          // ... and must stay below nlim
-    const uint8_t* my_ops = ops + lane * 16;
 
     auto tile_attend = [&](const TileCodes<NI, NS>& cd, const VRaw& vr, int t) __attribute__((always_inline)) {
         // ---- scores, keys as rows
@@ -1999,7 +2010,7 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
         for (int j = 0; j < KS; ++j) {
             const int u = j & 1;
             Op8 ahi, alo, thi, tlo;
-            const uint8_t* base = my_ops + (j * 4) * BLOCK;
+            const uint8_t* base = ops + (j * 4) * BLOCK + slot_pos(lane, j) * 16;
             *reinterpret_cast<uint4*>(ahi.u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
             *reinterpret_cast<uint4*>(alo.u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
             *reinterpret_cast<uint4*>(thi.u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
