@@ -60,6 +60,8 @@ def parse():
                          "outlier split, 32 hot channels at 3 bits + the rest at 2 (tq_query_transform_split "
                          "+ tq_score_split); fused: the whole decode step, tq_query_transform + "
                          "tq_score_attend (scores never written), against the two-call form")
+    ap.add_argument("--no-stream-probe", action="store_true",
+                    help="skip the same-size device-copy reference (for profiler runs of the kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -1051,11 +1053,12 @@ def main() -> int:
                           "launches of back-to-back transforms and back-to-back scores"),
         "ring_sets": len(ring),
     }
-    probe = stream_probe(device, alg_bytes)
-    probe["tq_score_frac_of_probe"] = achieved / probe["GB_s"]
-    out["stream_probe"] = probe
-    log(f"stream probe: {probe['bytes'] / 1e6:.1f} MB copied in {probe['us']:.2f} us ({probe['GB_s']:.0f} GB/s); "
-        f"tq_score at {probe['tq_score_frac_of_probe']:.2f} of it")
+    if not args.no_stream_probe:
+        probe = stream_probe(device, alg_bytes)
+        probe["tq_score_frac_of_probe"] = achieved / probe["GB_s"]
+        out["stream_probe"] = probe
+        log(f"stream probe: {probe['bytes'] / 1e6:.1f} MB copied in {probe['us']:.2f} us ({probe['GB_s']:.0f} GB/s); "
+            f"tq_score at {probe['tq_score_frac_of_probe']:.2f} of it")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
