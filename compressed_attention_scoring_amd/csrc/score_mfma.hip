@@ -984,28 +984,26 @@ __global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
                 gg = d0 / (kSplitDLo / 2);
                 blk16 = (d0 % (kSplitDLo / 2)) / SEG;
             }
-            uint8_t* lane_base = ops + (mtile * KS * 2) * BLOCK + (gg * 32 + rl) * 16;
+            // whole 16-byte slots (as prologue_store): the hot block fills slots 0 and 1
+            // in coordinate order, an other-instance block slots 2 + 2 blk16 + {0, 1} in
+            // the 2-bit order; slot positions swizzled by slot_pos
+            uint8_t* tile_base = ops + (mtile * KS * 2) * BLOCK;
+            const int pp = gg * 32 + rl;
+            uint16_t ah[SEG], al[SEG];
 #pragma unroll
-            for (int k = 0; k < SEG; ++k) {
-                int j, e;
-                if (hot) {
-                    j = k / 8;
-                    e = k % 8;
-                } else {
-                    mse_slot16<1, 2>(blk16, k, j, e);
-                    j += 2;
-                }
-                uint16_t hi, lo;
-                split_f16(a[k] * sr, hi, lo);
-                uint8_t* base = lane_base + (j * 2) * BLOCK + e * 2;
-                *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = hi;
-                *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = lo;
+            for (int k = 0; k < SEG; ++k) split_f16(a[k] * sr, ah[k], al[k]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int j = (hot ? 0 : 2 + 2 * blk16) + q;
+                uint8_t* base = tile_base + (j * 2) * BLOCK + slot_pos(pp, j) * 16;
+                const uint4 vh = hot ? whole_slot<0, 0, true>(ah, q) : whole_slot<1, 2, true>(ah, q);
+                const uint4 vl = hot ? whole_slot<0, 0, true>(al, q) : whole_slot<1, 2, true>(al, q);
+                *reinterpret_cast<uint4*>(base + 0 * BLOCK) = vh;
+                *reinterpret_cast<uint4*>(base + 1 * BLOCK) = vl;
             }
         }
     }
     __syncthreads();
-
-    const uint8_t* my_ops = ops + lane * 16;
 
     auto tile_scores = [&](const SplitTileCodes& c, int t) __attribute__((always_inline)) {
         f32x16 accH[MT], accL[MT];
@@ -1044,7 +1042,7 @@ __global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
             Op8 ahi[MT], alo[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* base = my_ops + ((mt * KS + j) * 2) * BLOCK;
+                const uint8_t* base = ops + ((mt * KS + j) * 2) * BLOCK + slot_pos(lane, j) * 16;
                 *reinterpret_cast<uint4*>(ahi[mt].u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
                 *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
             }
