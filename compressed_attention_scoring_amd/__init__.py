@@ -8,7 +8,7 @@ functions keep the C names:
     tq_score(A, T, keys, codebook)             -> scores
     tq_score_with_kernel(A, T, keys, codebook, kernel)
     tq_decode_debug(keys, D)                   -> (idx, sign, gamma)
-    tq_compress_keys(keys, Pi, S_mat, codebook, layout, bits) -> Keys
+    tq_compress_keys(keys, Pi, S_mat, codebook, layout, bits) -> Keys (with .norm)
     tq_attend(scores, values, codebook, Pi_v, scale) -> out
     tq_attend_workspace_bytes(P, B, S, D)
     tq_score_attend(A, T, keys, codebook, values, codebook_v, Pi_v, scale) -> out   (fused decode step)
@@ -73,6 +73,7 @@ class _CKeysOut(ctypes.Structure):
         ("idx", ctypes.c_void_p),
         ("sign", ctypes.c_void_p),
         ("gamma", ctypes.c_void_p),
+        ("norm", ctypes.c_void_p),
     ]
 
 
@@ -200,6 +201,9 @@ class Keys:
     sign: torch.Tensor
     gamma: torch.Tensor
     bits: int = 0
+    #: the keys' lengths ||k|| (gamma's dtype) when produced by tq_compress_keys, else None;
+    #: scores are against the unit keys, norm * score is the score against k as given
+    norm: torch.Tensor | None = None
 
     def _c(self, D: int):
         if self.layout == "unpacked":
@@ -314,7 +318,8 @@ def tq_decode_debug(keys: Keys, D: int, stream=None):
 
 def tq_compress_keys(keys: torch.Tensor, Pi: torch.Tensor, S_mat: torch.Tensor, codebook: torch.Tensor,
                      layout: str = "packed", bits: int = 3, stream=None) -> Keys:
-    """Compress float32 keys [P,S,D] (or [S,D]) with head p % H's Pi and S_mat into a new Keys."""
+    """Normalise and compress float32 keys [P,S,D] (or [S,D]) with head p % H's Pi and
+    S_mat into a new Keys; its ``norm`` holds the keys' lengths."""
     k3 = _as3(_gpu(keys, "keys", torch.float32))
     Pi3 = _as3(_gpu(Pi, "Pi", torch.float32))
     S3 = _as3(_gpu(S_mat, "S_mat", torch.float32))
@@ -338,14 +343,15 @@ def tq_compress_keys(keys: torch.Tensor, Pi: torch.Tensor, S_mat: torch.Tensor, 
         gamma = torch.empty((P, S), dtype=torch.float16, device=dev)
     else:
         raise ValueError(f"unknown layout {layout!r}")
-    out = _CKeysOut(lay, b, idx.data_ptr(), sign.data_ptr(), gamma.data_ptr())
+    norm = torch.empty_like(gamma)
+    out = _CKeysOut(lay, b, idx.data_ptr(), sign.data_ptr(), gamma.data_ptr(), norm.data_ptr())
     st = _stream(dev, stream)
     _check(_lib.tq_compress_keys(_ptr(k3), _ptr(Pi3), _ptr(S3), _ptr(codebook), codebook.numel(),
                                  ctypes.byref(out), P, H, S, D, st), "tq_compress_keys")
     squeeze = keys.dim() == 2
     if squeeze:
-        idx, sign, gamma = idx[0], sign[0], gamma[0]
-    return Keys(layout, idx, sign, gamma, bits=b)
+        idx, sign, gamma, norm = idx[0], sign[0], gamma[0], norm[0]
+    return Keys(layout, idx, sign, gamma, bits=b, norm=norm)
 
 
 @dataclass

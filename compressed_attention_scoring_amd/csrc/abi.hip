@@ -169,9 +169,9 @@ int tq_compress_keys(const float* keys, const float* Pi, const float* S_mat, con
     if (!keys || !Pi || !S_mat || !codebook || !out->idx || !out->sign || !out->gamma) return TQ_ERR_ARG;
     if (P > 65535 || !fits(P, S, D)) return TQ_ERR_UNSUPPORTED;
     if (!aligned16(keys) || !aligned16(Pi) || !aligned16(S_mat) || !aligned16(codebook) || !aligned16(out->idx) ||
-        !aligned16(out->sign) || !aligned16(out->gamma))
+        !aligned16(out->sign) || !aligned16(out->gamma) || (out->norm && !aligned16(out->norm)))
         return TQ_ERR_ALIGN;
-    const tq::KeyOut ko{static_cast<uint8_t*>(out->idx), static_cast<uint8_t*>(out->sign), out->gamma};
+    const tq::KeyOut ko{static_cast<uint8_t*>(out->idx), static_cast<uint8_t*>(out->sign), out->gamma, out->norm};
     const hipError_t e = tq::launch_compress(keys, Pi, S_mat, codebook, C, ko, out->layout, bits, P, H, S, D,
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;

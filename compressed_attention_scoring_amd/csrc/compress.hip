@@ -14,10 +14,12 @@
 // (78.6 TFLOP/s); the three D x D products per key run as v_mfma_f64_16x16x4_f64.
 //
 // One wavefront compresses 16 keys (the MFMA columns). Per tile:
-//   1. y = Pi k                 (A = Pi rows, B = the 16 keys)
+//   0. u = k / ||k||            (the page's "normalize, then rotate"; a zero key
+//                                stays the zero vector; ||k|| is stored if asked)
+//   1. y = Pi u                 (A = Pi rows, B = the 16 unit keys)
 //   2. idx = #{midpoints < y}, c = codebook[idx]
 //   3. x = Pi^T c               (A = Pi columns, B = c)
-//   4. r = k - x, gamma = ||r||
+//   4. r = u - x, gamma = ||r||
 //   5. p = S_mat r              (A = S_mat rows, B = r)
 //   6. sign = (p >= 0)          (a zero projection counts as +1)
 //   7. pack and store           (through LDS, one lane per 32 coordinates of a key)
@@ -66,7 +68,7 @@ template <int D, int LAYOUT, int BITS, int NC>
 __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     const float* __restrict__ keys, const float* __restrict__ Pi, const float* __restrict__ Smat,
     const float* __restrict__ codebook, int C, uint8_t* __restrict__ idx_out, uint8_t* __restrict__ sign_out,
-    void* __restrict__ gamma_out, int H, int S) {
+    void* __restrict__ gamma_out, void* __restrict__ norm_out, int H, int S) {
     constexpr int RB = D / 16;                 // 16-row output blocks
     constexpr int KQ = D / 16;                 // 16-wide contraction chunks (4 MFMAs each)
     using L = CompressLds<D>;
@@ -87,20 +89,39 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     uint8_t* ibuf = lds + wave * L::PER_WAVE;                  // [16][D] indices
     uint8_t* sbuf = ibuf + L::BYTES;                            // [16][D] sign bits (0/1)
 
-    // ---- 1. y = Pi k: B holds this lane's key at j = 16 kq + 4 q + t
+    // ---- 0. the key's length: this lane holds coordinates j = 16 kq + 4 q + t
+    //      (the order of the first product), the four lane groups the rest
+    float4 kv[KQ];
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) kv[kq] = *reinterpret_cast<const float4*>(kp + 16 * kq + 4 * q);
+    double nn = 0.0;
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+        nn = fma((double)kv[kq].x, (double)kv[kq].x, nn);
+        nn = fma((double)kv[kq].y, (double)kv[kq].y, nn);
+        nn = fma((double)kv[kq].z, (double)kv[kq].z, nn);
+        nn = fma((double)kv[kq].w, (double)kv[kq].w, nn);
+    }
+    nn += __shfl_xor(nn, 16);
+    nn += __shfl_xor(nn, 32);
+    const double nrm = sqrt(nn);
+    const double div = nrm > 0.0 ? nrm : 1.0;   // a zero key stays the zero vector
+
+    // ---- 1. y = Pi u: B holds this lane's unit key at j = 16 kq + 4 q + t
     f64x4 acc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb] = (f64x4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
-        const float4 kv = *reinterpret_cast<const float4*>(kp + 16 * kq + 4 * q);
+        const double u0 = (double)kv[kq].x / div, u1 = (double)kv[kq].y / div;
+        const double u2 = (double)kv[kq].z / div, u3 = (double)kv[kq].w / div;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const float4 av = *reinterpret_cast<const float4*>(Pp + (int64_t)(16 * rb + col) * D + 16 * kq + 4 * q);
-            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.x, (double)kv.x, acc[rb], 0, 0, 0);
-            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.y, (double)kv.y, acc[rb], 0, 0, 0);
-            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.z, (double)kv.z, acc[rb], 0, 0, 0);
-            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.w, (double)kv.w, acc[rb], 0, 0, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.x, u0, acc[rb], 0, 0, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.y, u1, acc[rb], 0, 0, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.z, u2, acc[rb], 0, 0, 0);
+            acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.w, u3, acc[rb], 0, 0, 0);
         }
     }
     // ---- 2. indices: acc[rb][v] = y[d = 16 rb + 4 v + q] of key col; the index
@@ -143,13 +164,14 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
                 acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)prow[16 * rb], cr[kq][t], acc[rb], 0, 0, 0);
         }
     }
-    // ---- 4. r = k - x (acc[rb][v] = x[j = 16 rb + 4 v + q] of key col), gamma
+    // ---- 4. r = u - x (acc[rb][v] = x[j = 16 rb + 4 v + q] of key col), gamma;
+    //      u is recomputed from the key in this order (the same division as above)
     double rr = 0.0;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            cr[rb][v] = (double)kp[16 * rb + 4 * v + q] - acc[rb][v];
+            cr[rb][v] = (double)kp[16 * rb + 4 * v + q] / div - acc[rb][v];
             rr = fma(cr[rb][v], cr[rb][v], rr);
         }
     }
@@ -191,7 +213,8 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
         const int u = pass * 64 + lane;
         const int kk = u / NB, blk = u % NB;
         const int s = s0 + kk;
-        const double gk = __shfl(gam, kk & 15);   // gamma of key kk sits in lane kk
+        const double gk = __shfl(gam, kk & 15);   // gamma and length of key kk sit in lane kk
+        const double nk = __shfl(nrm, kk & 15);
         if (kk < 16 && s < S) {
             const uint8_t* ib = ibuf + kk * D + 32 * blk;
             const uint8_t* sb = sbuf + kk * D + 32 * blk;
@@ -215,7 +238,10 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
                 uint4* sp = reinterpret_cast<uint4*>(sign_out + krow * D + 32 * blk);
                 sp[0] = make_uint4(so[0], so[1], so[2], so[3]);
                 sp[1] = make_uint4(so[4], so[5], so[6], so[7]);
-                if (blk == 0) reinterpret_cast<float*>(gamma_out)[krow] = (float)gk;
+                if (blk == 0) {
+                    reinterpret_cast<float*>(gamma_out)[krow] = (float)gk;
+                    if (norm_out) reinterpret_cast<float*>(norm_out)[krow] = (float)nk;
+                }
             } else {
                 // LSB-first bitstream: coordinate c of the block at bits [BITS c, BITS c + BITS)
                 uint32_t out[BITS] = {};
@@ -233,7 +259,10 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
 #pragma unroll
                 for (int c = 0; c < 32; ++c) sbits |= ((sw[c / 4] >> (8 * (c % 4))) & 1u) << c;
                 reinterpret_cast<uint32_t*>(sign_out + krow * (D / 8))[blk] = sbits;
-                if (blk == 0) reinterpret_cast<_Float16*>(gamma_out)[krow] = half_of(gk);
+                if (blk == 0) {
+                    reinterpret_cast<_Float16*>(gamma_out)[krow] = half_of(gk);
+                    if (norm_out) reinterpret_cast<_Float16*>(norm_out)[krow] = half_of(nk);
+                }
             }
         }
     }
@@ -247,10 +276,10 @@ hipError_t launch_compress_d(const float* keys, const float* Pi, const float* S_
     // codebook registers sized to the codebook: 8 entries cover every packed format
     if (C <= 8)
         hipLaunchKernelGGL((compress_kernel<D, LAYOUT, BITS, 8>), grid, dim3(kCompressWaves * 64), 0, stream,
-                           keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, H, S);
+                           keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, out.norm, H, S);
     else
         hipLaunchKernelGGL((compress_kernel<D, LAYOUT, BITS, kMaxCodebook>), grid, dim3(kCompressWaves * 64), 0,
-                           stream, keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, H, S);
+                           stream, keys, Pi, S_mat, codebook, C, out.idx, out.sign, out.gamma, out.norm, H, S);
     return hipGetLastError();
 }
 

@@ -41,25 +41,19 @@
 // mse_dim and qjl_dim.
 #include <type_traits>
 
+#include "mfma_ops.hpp"
 #include "tq_common.hpp"
 #include "value_sel.hpp"
 
 namespace tq {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace ops;
+
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kTileKeys = 32;
-constexpr uint32_t kOneOne = 0x3C003C00u;   // two f16 1.0
-constexpr uint32_t kSignBits = 0x80008000u;
-
-union Op8 {
-    f16x8 h;
-    uint32_t u[4];
-};
 
 // ---------------------------------------------------------------------------
 // Coordinate order. Element e (0..7) of k-step j of a lane half covers
@@ -269,24 +263,6 @@ static_assert(orders_are_bijections<1, 3, 32>() && orders_are_bijections<1, 3, 6
 // Key-side operand builders
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
-}
-
-// Four selector bytes (each < 8) -> two dwords of f16 pairs from a byte table
-// tab = {low bytes of entries 0-3, low bytes of 4-7, high bytes of 0-3, high bytes of 4-7}.
-__device__ __forceinline__ void lut4(uint32_t x, const uint32_t (&tab)[4], uint32_t& o0, uint32_t& o1) {
-    const uint32_t lo = perm(tab[1], tab[0], x);
-    const uint32_t hi = perm(tab[3], tab[2], x);
-    o0 = perm(hi, lo, 0x05010400u);
-    o1 = perm(hi, lo, 0x07030602u);
-}
-
-// (x & sign bits) | f16 1.0 pair in one v_bitop3_b32 (truth table 0xEA is
-// (S0 & S1) | S2): the sign bits of x become +-1.0 in both f16 halves.
-__device__ __forceinline__ uint32_t signs_of(uint32_t x) {
-    return __builtin_amdgcn_bitop3_b32(x, kSignBits, kOneOne, 0xEA);
-}
 
 template <int LAYOUT, int BITS>
 struct Fmt;
@@ -416,34 +392,6 @@ constexpr int align_of_seg(int row_bytes, int seg_bytes) {
          : (row_bytes % 8 == 0 && seg_bytes % 8 == 0) ? 8 : 4;
 }
 
-__device__ __forceinline__ float pow2_scale_for(float maxabs) {
-    // a power of two bringing maxabs into [2^13, 2^14); 1 if maxabs is 0 or not finite
-    if (!(maxabs > 0.f) || !(maxabs < 3.0e38f)) return 1.f;
-    int e;
-    (void)frexpf(maxabs, &e);   // maxabs = f * 2^e, f in [0.5, 1)
-    return ldexpf(1.f, 14 - e);
-}
-
-__device__ __forceinline__ void split_f16(float x, uint16_t& hi, uint16_t& lo) {
-    const _Float16 h = (_Float16)x;
-    const _Float16 l = (_Float16)(x - (float)h);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, l);
-}
-
-// Score stores go through a raw buffer descriptor covering the valid rows of one
-// 32-query tile of the output, so the hardware drops writes to rows past B.
-// Keys past S get a lane offset of 2^31, beyond any descriptor here. Every store
-// therefore issues on every path, with no branches, which keeps the compiler's
-// count of outstanding memory operations exact: a wait for the next tile's codes
-// does not also wait for this tile's stores to reach memory.
-// Byte offsets are row * S * 4 + key * 4 with row < 32; the caller keeps
-// S < 2^24, so every in-range offset is below 2^31 and an out-of-range key's
-// offset (2^31 plus a row offset below 2^31) cannot wrap around.
-constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit buffer, gfx9 family
-constexpr uint32_t kDropKey = 0x80000000u;       // lane offset of a key past S
-constexpr int kNonTemporal = 2;                  // cache policy: stream past the caches
-
 // Byte offset of this lane's key in row 4 * g of a tile (g = lane / 32), or
 // kDropKey past the last key; output element v then adds row_offset(v, S).
 __device__ __forceinline__ uint32_t lane_offset(int s, int S, int g) {
@@ -454,39 +402,7 @@ __device__ __forceinline__ uint32_t row_offset(int v, int S) {
     return (uint32_t)(8 * (v >> 2) + (v & 3)) * (uint32_t)S * 4u;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t score_rows(float* base, int rows, int S) {
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)((uint32_t)rows * (uint32_t)S * 4u), kBufferWord3);
-}
 
-__device__ __forceinline__ void store_score(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kNonTemporal);
-}
-
-// Codebook byte tables for lut4: the entries (up to 8, zero beyond C) times a
-// power of two sc, split into f16 hi and lo parts.
-__device__ __forceinline__ void codebook_tables(const float* __restrict__ codebook, int C, float& sc,
-                                                uint32_t (&tab_hi)[4], uint32_t (&tab_lo)[4]) {
-    float cbv[8];
-    float mc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        cbv[k] = k < C ? codebook[k] : 0.f;
-        mc = fmaxf(mc, fabsf(cbv[k]));
-    }
-    sc = pow2_scale_for(mc);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) tab_hi[w] = tab_lo[w] = 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint16_t hb, lb;
-        split_f16(cbv[k] * sc, hb, lb);
-        const int w = k >> 2, sh = 8 * (k & 3);
-        tab_hi[w] |= (uint32_t)(hb & 0xffu) << sh;
-        tab_hi[2 + w] |= (uint32_t)(hb >> 8) << sh;
-        tab_lo[w] |= (uint32_t)(lb & 0xffu) << sh;
-        tab_lo[2 + w] |= (uint32_t)(lb >> 8) << sh;
-    }
-}
 
 // One 32-key tile's compressed codes for this lane: its segment of the key's
 // index and sign streams, and the key's gamma.
@@ -747,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         const float sA = pow2_scale_for(ma);
         const float sT = pow2_scale_for(mt);
         // sA, sT and sc are powers of two, so these factors are exact
-        if (row < MT * 32 && pl == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
+        if (row < MT * 32 && pl == 0) rowk[row] = make_float2(inv_scales(sA, sc), coef / sT);
         const int mtile = row / 32, rl = row % 32;
         const int d0 = pl * SEG;
         const int gg = d0 / HALF;                               // lane segment holding these coordinates
@@ -893,11 +809,6 @@ __device__ __forceinline__ void split_hot_groups(const SplitTileCodes& c, int g,
     v1 = (g ? (c.h1 >> 8) : __builtin_amdgcn_alignbit(c.h1, c.h0, 24u)) & 0xFFFFFFu;
 }
 
-// Selector bytes of four consecutive 3-bit fields of v (fields 0-3 of v).
-__device__ __forceinline__ uint32_t sel3x4(uint32_t v) {
-    return (v & 7u) | ((v << 5) & 0x700u) | ((v << 10) & 0x70000u) | ((v << 15) & 0x7000000u);
-}
-
 template <int MT>
 __global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
     const float* __restrict__ A_hi, const float* __restrict__ A_lo,
@@ -971,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
         }
         const float sh = pow2_scale_for(mh);
         const float sl = pow2_scale_for(ml);
-        if (row < MT * 32 && pl == 0) rowk[row] = make_float2(1.f / (sh * sch), 1.f / (sl * scl));
+        if (row < MT * 32 && pl == 0) rowk[row] = make_float2(inv_scales(sh, sch), inv_scales(sl, scl));
         if (row < MT * 32) {
             const int mtile = row / 32, rl = row % 32;
             const float sr = hot ? sh : sl;
@@ -1179,7 +1090,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float sA = pow2_scale_for(ma);
         const float sT = pow2_scale_for(mt);
-        if (g == 0) rowk[wave][qt * 32 + col] = make_float2(1.f / (sA * sc), coef / sT);
+        if (g == 0) rowk[wave][qt * 32 + col] = make_float2(inv_scales(sA, sc), coef / sT);
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
 #pragma unroll
@@ -1374,7 +1285,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float sA = pow2_scale_for(ma);
     const float sT = pow2_scale_for(mt);
-    if (g == 0) rowk[wave][col] = make_float2(1.f / (sA * sc), coef / sT);
+    if (g == 0) rowk[wave][col] = make_float2(inv_scales(sA, sc), coef / sT);
     Op8 ahi[KS], alo[KS], thi[QT], tlo[QT];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
@@ -1561,7 +1472,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     // its T scale in row 4 gq + 2
     const float sA_out = __shfl(s_row, 4 * gq);
     const float sT_out = __shfl(s_row, 4 * gq + 2);
-    const float kx = 1.f / (sA_out * sc);
+    const float kx = inv_scales(sA_out, sc);
     const float ky = coef / sT_out;
 
     // operands: for k-step j, ops[j][0] and [1] pair codebook-hi elements 0-3
@@ -1945,7 +1856,7 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
         }
         const float sA = pow2_scale_for(ma);
         const float sT = pow2_scale_for(mt);
-        if (row < 32 && pl == 0) rowk[row] = make_float2(1.f / (sA * sc), coef / sT);
+        if (row < 32 && pl == 0) rowk[row] = make_float2(inv_scales(sA, sc), coef / sT);
         {
             const int d0 = pl * SEG;
             const int gg = d0 / HALF;

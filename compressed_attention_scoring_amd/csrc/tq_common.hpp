@@ -54,6 +54,7 @@ struct KeyOut {
     uint8_t* idx;
     uint8_t* sign;
     void* gamma;
+    void* norm;   // the keys' lengths in gamma's dtype, or null
 };
 bool compress_supported(int layout, int bits, int C, int D);
 hipError_t launch_compress(const float* keys, const float* Pi, const float* S_mat, const float* codebook,

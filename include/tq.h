@@ -177,7 +177,7 @@ int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out,
 
 /*
  * Output descriptor of tq_compress_keys: the same layouts as tq_keys, with
- * writable device pointers.
+ * writable device pointers, and an optional output of the keys' lengths.
  */
 typedef struct tq_keys_out {
     int32_t layout;   /* TQ_UNPACKED or TQ_PACKED */
@@ -185,18 +185,23 @@ typedef struct tq_keys_out {
     void* idx;
     void* sign;
     void* gamma;
+    void* norm;       /* NULL, or [P, S] lengths ||k|| in gamma's dtype (float32
+                         unpacked, float16 packed) */
 } tq_keys_out;
 
 /*
  * tq_compress_keys: compress keys into either layout above (the inner-product
  * quantizer of "TurboQuant: Rotate-then-Quantize KV Caches at 3 Bits",
  * section 3, with the residual norm of "TurboQuant Attention in CUDA",
- * section "The keys arrived in pieces"). For each key k of problem p, with
- * head h = p % H:
- *   y = Pi_h k;  idx_d = number of codebook midpoints strictly below y_d
- *   (a value on a midpoint takes the lower index);  r = k - Pi_h^T c[idx];
- *   gamma = ||r||;  sign_d = +1 if (S_h r)_d >= 0 else -1.
- * Keys are compressed as given: the method assumes unit keys (normalise first).
+ * section "The keys arrived in pieces"), normalising first as that page's
+ * section 3 orders it. For each key k of problem p, with head h = p % H:
+ *   u = k / ||k|| (a zero key is compressed as the zero vector);
+ *   y = Pi_h u;  idx_d = number of codebook midpoints strictly below y_d
+ *   (a value on a midpoint takes the lower index);  r = u - Pi_h^T c[idx];
+ *   gamma = ||r||;  sign_d = +1 if (S_h r)_d >= 0 else -1;
+ *   norm = ||k|| if out->norm is not NULL.
+ * tq_score's scores are against the unit key u; multiplying them by the
+ * stored norm gives scores against k as given.
  *
  *   keys      float32 [P, S, D]
  *   Pi, S_mat float32 [H, D, D]   (the matrices tq_query_transform takes)

@@ -10,8 +10,14 @@ dequantizes as Pi^T c[idx].
 
 "TurboQuant Attention in CUDA: Transform the Query, Reuse the Work", section
 "The keys arrived in pieces": gamma is the length of the residual left after
-subtracting the centroid-based approximation, not the key's length. The keys
-here are unit vectors, so no key norm is stored.
+subtracting the centroid-based approximation, not the key's length.
+
+:func:`quantize_prod` is the whole store-side step as the kanthi.in page's
+section 3 orders it ("normalize, then rotate"): each key is divided by its
+length first (a zero key stays the zero vector), the unit key is compressed by
+:func:`quantize_prod_unit`, and the length is returned beside the codes. The
+scores the path computes are against the unit key; the length is what a caller
+multiplies back for scores against the key as given.
 
 The sign of an exactly zero projection is taken as +1, so every stored sign is
 +-1 (the page's ``np.sign`` would give 0 there; the case has probability zero).
@@ -57,3 +63,14 @@ def quantize_prod_unit(keys: np.ndarray, Pi: np.ndarray, S_mat: np.ndarray,
     proj = r @ np.asarray(S_mat, np.float64).T          # (S_mat r_s) for each key
     sign = np.where(proj >= 0.0, 1, -1).astype(np.int8)
     return idx, sign, gamma
+
+
+def quantize_prod(keys: np.ndarray, Pi: np.ndarray, S_mat: np.ndarray, codebook: np.ndarray):
+    """Normalise, then compress keys [S, D] of any length into (idx uint8 [S, D],
+    sign int8 [S, D], gamma float64 [S], norm float64 [S]); a zero key is
+    compressed as the zero vector and gets norm 0."""
+    k = np.asarray(keys, np.float64)
+    norm = np.sqrt(np.sum(k * k, axis=1))
+    unit = k / np.where(norm > 0.0, norm, 1.0)[:, None]
+    idx, sign, gamma = quantize_prod_unit(unit, Pi, S_mat, codebook)
+    return idx, sign, gamma, norm

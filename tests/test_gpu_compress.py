@@ -1,6 +1,7 @@
-"""tq_compress_keys against the oracle compressor (oracle.compress then
-oracle.pack): indices and signs bit-exact, gamma equal after its single
-rounding (float32 unpacked, binary16 packed). Both sides take the index and
+"""tq_compress_keys against the oracle compressor (oracle.compress.quantize_prod,
+which normalises each key first, then oracle.pack): indices and signs
+bit-exact, gamma and the key lengths equal after their single rounding
+(float32 unpacked, binary16 packed). Both sides take the index and
 sign decisions in float64, so they agree except within rounding distance of a
 midpoint or of a zero projection (probability about 1e-15 per coordinate).
 Then compress-then-score on the GPU against the oracle's reconstruction."""
@@ -28,23 +29,29 @@ def make_case(seed: int, P: int, H: int, S: int, D: int, C: int, family: str = "
     return keys, Pi, S_mat, codebook_fp32(D, C)
 
 
-def oracle_compress(keys32, Pi, S_mat, cb, H):
+def oracle_compress(keys32, Pi, S_mat, cb, H, with_norm=False):
     """The oracle on the float32 keys the GPU sees (widened to float64)."""
-    out = [oc.quantize_prod_unit(keys32[p].astype(np.float64), Pi[p % H], S_mat[p % H], cb)
+    out = [oc.quantize_prod(keys32[p].astype(np.float64), Pi[p % H], S_mat[p % H], cb)
            for p in range(keys32.shape[0])]
-    return (np.stack([o[0] for o in out]), np.stack([o[1] for o in out]), np.stack([o[2] for o in out]))
+    res = tuple(np.stack([o[i] for o in out]) for i in range(4))
+    return res if with_norm else res[:3]
 
 
-def check_equal(kg: tq.Keys, idx_u, sign_u, gamma, layout, bits):
+def check_equal(kg: tq.Keys, idx_u, sign_u, gamma, layout, bits, norm=None):
     gi, gs, gg = kg.idx.cpu().numpy(), kg.sign.cpu().numpy(), kg.gamma.cpu().numpy()
+    gn = kg.norm.cpu().numpy()
     if layout == "unpacked":
         np.testing.assert_array_equal(gi, idx_u)
         np.testing.assert_array_equal(gs, sign_u)
         np.testing.assert_array_equal(gg, gamma.astype(np.float32))
+        if norm is not None:
+            np.testing.assert_array_equal(gn, norm.astype(np.float32))
     else:
         np.testing.assert_array_equal(gi, opk.pack_indices(idx_u, bits))
         np.testing.assert_array_equal(gs, opk.pack_signs(sign_u))
         np.testing.assert_array_equal(gg.view(np.uint16), opk.gamma_to_half(gamma).view(np.uint16))
+        if norm is not None:
+            np.testing.assert_array_equal(gn.view(np.uint16), opk.gamma_to_half(norm).view(np.uint16))
 
 
 CASES = [
@@ -109,3 +116,27 @@ def test_compress_empty_and_tail():
     check_equal(kg, idx_u, sign_u, gamma, "unpacked", 0)
     empty = tq.tq_compress_keys(t(keys[:, :0]), t(Pi), t(S_mat), t(cb), "packed", 2)
     assert empty.idx.shape == (1, 0, 32)
+
+
+@pytest.mark.parametrize("layout,bits,C,D", [("unpacked", 0, 4, 128), ("packed", 2, 4, 128), ("packed", 3, 8, 64)])
+def test_compress_normalises_keys_of_any_length(layout, bits, C, D):
+    """Keys of lengths from 1e-3 to 1e3 and an all-zero key: the codes are those of
+    the unit keys (the oracle normalises first), the stored norm is the length."""
+    say(f"compress non-unit keys {layout} bits={bits} C={C} D={D}")
+    rng = np.random.default_rng([41, D, C])
+    P, H, S = 2, 1, 150
+    Pi, S_mat = synth.head_matrices(41, H, D)
+    cb = codebook_fp32(D, C)
+    keys = rng.standard_normal((P, S, D)) * np.exp(rng.uniform(np.log(1e-3), np.log(1e3), size=(P, S, 1)))
+    keys[0, 7] = 0.0
+    keys = keys.astype(np.float32)
+    kg = tq.tq_compress_keys(t(keys), t(Pi), t(S_mat), t(cb), layout, bits)
+    torch.cuda.synchronize()
+    idx_u, sign_u, gamma, norm = oracle_compress(keys, Pi, S_mat, cb, H, with_norm=True)
+    assert norm[0, 7] == 0.0
+    check_equal(kg, idx_u, sign_u, gamma, layout, bits, norm)
+    # the unit-length keys compress to the same codes
+    unit = (keys.astype(np.float64) / np.maximum(norm, 1e-300)[..., None]).astype(np.float32)
+    kg1 = tq.tq_compress_keys(t(unit), t(Pi), t(S_mat), t(cb), layout, bits)
+    same = (kg1.idx.cpu().numpy() == kg.idx.cpu().numpy()).mean()
+    assert same > 0.999, same

@@ -122,3 +122,32 @@ def test_inner_product_unbiased_over_projections():
     # the MSE stage alone is biased for this pair: the test can tell
     est0, _, _ = _qjl_trials(q, k, Pi, cb, rng, 200, D, with_qjl=False)
     assert abs(est0.mean() - true) > 50 * math.sqrt(var / M)
+
+
+def test_normalise_then_compress():
+    """quantize_prod divides by the length first: unit keys give quantize_prod_unit's
+    codes and norm 1; a key scaled by any a > 0 gives the same codes and a times the
+    norm; a zero key is the zero vector (indices of 0, gamma = 0) with norm 0."""
+    rng = np.random.default_rng(31)
+    D = 64
+    Pi = synth.haar_rotation(rng, D)
+    S_mat = synth.gaussian_projection(rng, D)
+    cb = ocb.codebook_fp32(D, 4)
+    k = synth.unit_keys(rng, 50, D, "outlier")
+    i0, s0, g0 = ocp.quantize_prod_unit(k, Pi, S_mat, cb)
+    i1, s1, g1, n1 = ocp.quantize_prod(k, Pi, S_mat, cb)
+    np.testing.assert_array_equal(i1, i0)
+    np.testing.assert_array_equal(s1, s0)
+    np.testing.assert_allclose(g1, g0, rtol=1e-14)
+    np.testing.assert_allclose(n1, 1.0, rtol=1e-14)
+    scale = rng.uniform(0.01, 100.0, size=50)
+    i2, s2, g2, n2 = ocp.quantize_prod(k * scale[:, None], Pi, S_mat, cb)
+    np.testing.assert_array_equal(i2, i0)
+    np.testing.assert_array_equal(s2, s0)
+    np.testing.assert_allclose(g2, g0, rtol=1e-12)
+    np.testing.assert_allclose(n2, scale, rtol=1e-14)
+    iz, sz, gz, nz = ocp.quantize_prod(np.zeros((1, D)), Pi, S_mat, cb)
+    np.testing.assert_array_equal(iz, ocp.nearest_indices(np.zeros((1, D)), cb))
+    assert nz[0] == 0.0
+    # the residual of the zero vector is minus the centroid rebuild
+    np.testing.assert_allclose(gz[0], np.linalg.norm(ocp.dequantize_mse(iz, Pi, cb)[0]), rtol=1e-14)
