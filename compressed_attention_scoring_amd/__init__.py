@@ -36,9 +36,9 @@ import torch
 
 __all__ = [
     "Keys", "Values", "TqError", "tq_attend", "tq_attend_workspace_bytes", "tq_query_transform_hadamard",
-    "tq_score_mse", "tq_score_attend", "tq_score_attend_workspace_bytes", "SplitKeys", "tq_query_transform_split", "tq_score_split", "tq_query_transform", "tq_score", "tq_score_with_kernel",
+    "tq_score_mse", "tq_score_attend", "tq_attend_no_alloc", "tq_score_attend_workspace_bytes", "SplitKeys", "tq_query_transform_split", "tq_score_split", "tq_query_transform", "tq_score", "tq_score_with_kernel",
     "tq_decode_debug", "tq_compress_keys", "tq_score_kernel_name", "tq_status_string", "library_path",
-    "TQ_UNPACKED", "TQ_PACKED", "KERNELS", "TQ_OK", "TQ_ERR_ARG", "TQ_ERR_UNSUPPORTED", "TQ_ERR_ALIGN",
+    "TQ_UNPACKED", "TQ_PACKED", "KERNELS", "TQ_OK", "TQ_ERR_ARG", "TQ_ERR_UNSUPPORTED", "TQ_ERR_ALIGN", "TQ_NO_ALLOC_SCRATCH_BYTES",
     "TQ_ERR_LAUNCH",
 ]
 
@@ -51,6 +51,8 @@ TQ_ERR_ARG = -1
 TQ_ERR_UNSUPPORTED = -2
 TQ_ERR_ALIGN = -3
 TQ_ERR_LAUNCH = -4
+#: bytes of the per-GPU scratch tq_attend_no_alloc uses as its workspace (tq.h)
+TQ_NO_ALLOC_SCRATCH_BYTES = 48 * 1024 * 1024
 TQ_UNPACKED = 0
 TQ_PACKED = 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_lds": 3, "mfma_reg": 4, "mfma16": 5, "mfma_shared": 6}
@@ -115,6 +117,9 @@ def _load():
     lib.tq_attend.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp, vp, ctypes.c_size_t,
                               i32, i32, i32, i32, i32, vp]
     lib.tq_attend.restype = i32
+    lib.tq_attend_no_alloc.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp,
+                                       i32, i32, i32, i32, i32, vp]
+    lib.tq_attend_no_alloc.restype = i32
     lib.tq_score_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.tq_score_attend_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_score_attend.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, ctypes.POINTER(_CValues), vp, i32, vp,
@@ -429,6 +434,36 @@ def tq_attend(scores: torch.Tensor, values: Values, codebook: torch.Tensor, Pi_v
     _check(_lib.tq_attend(_ptr(s3), ctypes.byref(cv), _ptr(codebook), codebook.numel(), _ptr(Pv),
                           float(scale), _ptr(out), _ptr(workspace), workspace.numel(), P, H, B, S, D, st),
            "tq_attend")
+    return out.view(B, D) if squeeze else out.view(P, B, D)
+
+
+def tq_attend_no_alloc(scores: torch.Tensor, values: Values, codebook: torch.Tensor, Pi_v: torch.Tensor,
+                       scale: float | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """tq_attend with the library's fixed per-GPU scratch as workspace (no allocation
+    inside the call; pass ``out`` to allocate nothing at all). Calls that may overlap
+    on one GPU race on the scratch."""
+    squeeze = scores.dim() == 2
+    s3 = _as3(_gpu(scores, "scores", torch.float32))
+    Pv = _as3(_gpu(Pi_v, "Pi_v", torch.float32))
+    _gpu(codebook, "codebook", torch.float32)
+    P, B, S = s3.shape
+    H, D = Pv.shape[0], Pv.shape[-1]
+    if Pv.shape != (H, D, D):
+        raise ValueError("Pi_v must be [H, D, D]")
+    cv, Pk, Sk = values._c(D)
+    if (Pk, Sk) != (P, S):
+        raise ValueError(f"values hold [P={Pk}, S={Sk}], scores [P={P}, S={S}]")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dev = scores.device
+    if out is None:
+        out = torch.empty((P, B, D), dtype=torch.float32, device=dev)
+    _gpu(out, "out", torch.float32)
+    if out.numel() != P * B * D:
+        raise ValueError("out must hold P*B*D floats")
+    st = _stream(dev, stream)
+    _check(_lib.tq_attend_no_alloc(_ptr(s3), ctypes.byref(cv), _ptr(codebook), codebook.numel(), _ptr(Pv),
+                                   float(scale), _ptr(out), P, H, B, S, D, st), "tq_attend_no_alloc")
     return out.view(B, D) if squeeze else out.view(P, B, D)
 
 

@@ -3,6 +3,8 @@
 // contract of each entry point.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tq.h"
 #include "tq_common.hpp"
 
@@ -78,6 +80,35 @@ int pick_kernel(int layout, int bits, int C, int B, int S, int D) {
     return mfma_ok(layout, bits, C, B, S, D) ? TQ_KERNEL_MFMA : TQ_KERNEL_VALU;
 }
 
+}  // namespace
+
+namespace {
+// Workspace of tq_attend_no_alloc: a file-scope device array, one copy per GPU
+// (the code object's own storage, which lives as long as the process). Host
+// code never passes `scratch` itself to a kernel -- in host code the name is a
+// stand-in, not a device address -- but the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = TQ_NO_ALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address in *out; TQ_ERR_LAUNCH if HIP cannot
+// name the device or the symbol.
+int current_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TQ_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TQ_ERR_LAUNCH;
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return TQ_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -205,6 +236,28 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
                                            static_cast<float*>(workspace), P, H, B, S, D,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_attend_no_alloc(const float* scores, const tq_values* values, const float* codebook, int C,
+                       const float* Pi_v, float scale, float* out, int P, int H, int B, int S, int D,
+                       void* stream) {
+    // the shape checks of tq_attend come first, so errors match it
+    if (!values || P < 0 || B < 0 || S < 0 || H <= 0 || D <= 0 || P % H != 0) return TQ_ERR_ARG;
+    if (values->layout != TQ_UNPACKED && values->layout != TQ_PACKED) return TQ_ERR_ARG;
+    const int bits = values->layout == TQ_PACKED ? values->bits : 0;
+    if (values->layout == TQ_PACKED && ((bits != 2 && bits != 3) || C != (1 << bits))) return TQ_ERR_UNSUPPORTED;
+    if (!tq::attend_supported(values->layout, bits, C, D)) return TQ_ERR_UNSUPPORTED;
+    if (P == 0 || B == 0) return TQ_OK;
+    if (S == 0) return TQ_ERR_ARG;
+    if (P > 65535 || B > 262144 || !fits(P, B, S) || !fits(P, S, D)) return TQ_ERR_UNSUPPORTED;
+    const size_t need = tq_attend_workspace_bytes(P, B, S, D);
+    if (need == 0 || need > kNoAllocScratchBytes) return TQ_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    const int rc = current_scratch(&ws);
+    if (rc != TQ_OK) return rc;
+    // every partial record the combine reads is written first by the partial
+    // kernel, so nothing in the scratch has to start at zero
+    return tq_attend(scores, values, codebook, C, Pi_v, scale, out, ws, kNoAllocScratchBytes, P, H, B, S, D, stream);
 }
 
 namespace {

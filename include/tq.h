@@ -281,6 +281,24 @@ int tq_attend(const float* scores, const tq_values* values, const float* codeboo
               const float* Pi_v, float scale, float* out, void* workspace, size_t workspace_bytes,
               int P, int H, int B, int S, int D, void* stream);
 
+/*
+ * tq_attend_no_alloc: tq_attend for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, result and errors as tq_attend, without the workspace: the
+ * partial results go to a fixed scratch array in device memory that the
+ * library holds per GPU for the life of the process (TQ_NO_ALLOC_SCRATCH_BYTES,
+ * 48 MiB). It calls no allocating routine. Shapes whose workspace
+ * (tq_attend_workspace_bytes) exceeds the scratch are TQ_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams, or host threads without ordering) race and must
+ * not be issued; calls ordered on one stream are fine. TQ_ERR_LAUNCH if the
+ * scratch's device address cannot be obtained.
+ */
+#define TQ_NO_ALLOC_SCRATCH_BYTES (48u * 1024u * 1024u)
+int tq_attend_no_alloc(const float* scores, const tq_values* values, const float* codebook, int C,
+                       const float* Pi_v, float scale, float* out, int P, int H, int B, int S, int D,
+                       void* stream);
+
 /* forms of the fused decode step; TQ_ATTEND_AUTO picks by shape */
 #define TQ_ATTEND_AUTO     0
 #define TQ_ATTEND_FUSED    1  /* one pass: scores never written */

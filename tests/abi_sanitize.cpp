@@ -186,6 +186,15 @@ void attention() {
     EXPECT(tq_attend(F, &vu, F, 4, F, 1.f, F, V, SIZE_MAX, 65535, 1, 262144, INT_MAX, 128, nullptr),
            TQ_ERR_UNSUPPORTED);
     EXPECT(tq_attend(F, &vu, F, 4, F, 1.f, M, V, SIZE_MAX, 1, 1, 1, 1, 128, nullptr), TQ_ERR_ALIGN);
+    // the allocation-free form: the same argument checks, then the scratch bound,
+    // all before any device call
+    EXPECT(tq_attend_no_alloc(F, nullptr, F, 4, F, 1.f, F, 1, 1, 1, 1, 128, nullptr), TQ_ERR_ARG);
+    EXPECT(tq_attend_no_alloc(F, &vu, F, 4, F, 1.f, F, 1, 0, 1, 1, 128, nullptr), TQ_ERR_ARG);
+    EXPECT(tq_attend_no_alloc(F, &v2, F, 8, F, 1.f, F, 1, 1, 1, 1, 128, nullptr), TQ_ERR_UNSUPPORTED);
+    EXPECT(tq_attend_no_alloc(F, &vu, F, 4, F, 1.f, F, 0, 1, 1, 1, 128, nullptr), TQ_OK);
+    EXPECT(tq_attend_no_alloc(F, &vu, F, 4, F, 1.f, F, 1, 1, 1, 0, 128, nullptr), TQ_ERR_ARG);
+    EXPECT(tq_attend_no_alloc(F, &vu, F, 4, F, 1.f, F, 1, 1, 262144, 1000, 128, nullptr), TQ_ERR_UNSUPPORTED);
+    EXPECT(tq_attend_no_alloc(F, &vu, F, 4, F, 1.f, F, 65535, 1, 262144, INT_MAX, 128, nullptr), TQ_ERR_UNSUPPORTED);
 
     EXPECT(tq_score_attend_with_mode(F, F, &p3, F, 8, &v2, F, 4, F, 1.f, F, V, SIZE_MAX, 1, 1, 32, 100, 128, 5,
                                      nullptr), TQ_ERR_ARG);

@@ -13,7 +13,7 @@ EXPECTED = {
     "tq_query_transform", "tq_score", "tq_score_with_kernel", "tq_score_kernel_name",
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
     "tq_query_transform_hadamard", "tq_score_mse", "tq_query_transform_split", "tq_score_split",
-    "tq_score_attend", "tq_score_attend_workspace_bytes", "tq_score_attend_with_mode",
+    "tq_score_attend", "tq_score_attend_workspace_bytes", "tq_score_attend_with_mode", "tq_attend_no_alloc",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
