@@ -61,7 +61,7 @@ def parse():
                          "+ tq_score_split); fused: the whole decode step, tq_query_transform + "
                          "tq_score_attend (scores never written), against the two-call form")
     ap.add_argument("--no-stream-probe", action="store_true",
-                    help="skip the same-size device-copy reference (for profiler runs of the kernels)")
+                    help="skip the streaming probes and the same-size device copy (for profiler runs of the kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (profiling runs)")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly (no HIP graphs)")
@@ -246,6 +246,86 @@ def stream_probe(device, nbytes: int) -> dict:
     us = 1e3 * e0.elapsed_time(e1) / (reps * npairs)
     return {"kind": "device-to-device copy (torch copy_), graph-replayed over distinct buffers",
             "bytes": 2 * half, "us": us, "GB_s": 2 * half / (us * 1e-6) / 1e9}
+
+
+def stream_probes(device, read_bytes: int, write_bytes: int, steps: int) -> dict:
+    """The library's streaming probes at the workload's byte counts: tq_probe_read
+    over read_bytes (the key codes of one launch), tq_probe_write over
+    write_bytes (its scores), and tq_probe_read_write (each workgroup reads its
+    slice of the codes, then writes its slice of the scores from what it read).
+    Each is launched over a ring of distinct buffers (>= 512 MB, so no launch
+    finds its bytes in the caches), captured in a graph and replayed back to
+    back, timed with HIP events on the launching stream -- the same method as
+    the score kernel's figure."""
+    import ctypes
+
+    import torch
+
+    import compressed_attention_scoring_amd as tq
+
+    rb = (read_bytes + 15) // 16 * 16
+    wb = (write_bytes + 15) // 16 * 16
+    npairs = max(2, min(64, math.ceil(RING_BYTES / (rb + wb))))
+    pairs = [(torch.empty(rb, dtype=torch.uint8, device=device), torch.empty(wb, dtype=torch.uint8, device=device))
+             for _ in range(npairs)]
+    for src, _ in pairs:
+        src.fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device=device)
+    lib = tq._lib
+    vp = ctypes.c_void_p
+
+    def launch(kind, src, dst):
+        st = vp(torch.cuda.current_stream(device).cuda_stream)
+        if kind == "read":
+            rc = lib.tq_probe_read(vp(src.data_ptr()), ctypes.c_size_t(rb), vp(sink.data_ptr()), st)
+        elif kind == "write":
+            rc = lib.tq_probe_write(vp(dst.data_ptr()), ctypes.c_size_t(wb), st)
+        else:
+            rc = lib.tq_probe_read_write(vp(src.data_ptr()), ctypes.c_size_t(rb), vp(dst.data_ptr()),
+                                         ctypes.c_size_t(wb), st)
+        if rc != 0:
+            raise tq.TqError(rc, f"tq_probe_{kind}")
+
+    out = {"kind": "the library's streaming probe kernels (tq_probe_*), graph-replayed over distinct buffers, "
+                   "HIP events",
+           "ring_pairs": npairs}
+    reps = max(2, steps // npairs)
+    for kind, nbytes in (("read", rb), ("write", wb), ("read_write", rb + wb)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for src, dst in pairs:
+                launch(kind, src, dst)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / (reps * npairs)
+        out[kind] = {"bytes": nbytes, "us": us, "GB_s": nbytes / (us * 1e-6) / 1e9}
+    return out
+
+
+def trace_record(w, kname):
+    """Per-dispatch durations of this workload's score kernel from the committed
+    rocprofv3 kernel-trace record, if it was taken on the kernel that runs now
+    with its source as it is now; else None."""
+    import hashlib
+
+    try:
+        with open(os.path.join(ROOT, "profiles", f"tq_score_{w.name}_kernel_trace.json")) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for p in rec["source_files"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    if h.hexdigest() != rec.get("source_sha256") or rec.get("kernel_id") != kname:
+        return None
+    return rec
 
 
 def cpu_baseline(w, host, target_s):
@@ -1053,11 +1133,24 @@ def main() -> int:
                           "launches of back-to-back transforms and back-to-back scores"),
         "ring_sets": len(ring),
     }
+    rec = trace_record(w, kname)
+    if rec is not None:
+        med = rec["per_dispatch_us"]["median"]
+        out["roofline"]["trace"] = {"source": rec["profile"], "median_us": med, "avg_us": rec["per_dispatch_us"]["avg"],
+                                    "frac_at_median": alg_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS}
     if not args.no_stream_probe:
+        probes = stream_probes(device, w.key_bytes(), w.score_bytes(), args.steps)
+        rw = probes["read_write"]
+        probes["tq_score_time_over_read_write"] = score_us / rw["us"]
+        out["stream_probes"] = probes
+        log(f"probes: read {probes['read']['bytes'] / 1e6:.2f} MB in {probes['read']['us']:.2f} us, "
+            f"write {probes['write']['bytes'] / 1e6:.2f} MB in {probes['write']['us']:.2f} us, "
+            f"read-then-write {rw['us']:.2f} us ({rw['GB_s']:.0f} GB/s); tq_score takes "
+            f"{probes['tq_score_time_over_read_write']:.2f}x the read-then-write probe")
         probe = stream_probe(device, alg_bytes)
         probe["tq_score_frac_of_probe"] = achieved / probe["GB_s"]
         out["stream_probe"] = probe
-        log(f"stream probe: {probe['bytes'] / 1e6:.1f} MB copied in {probe['us']:.2f} us ({probe['GB_s']:.0f} GB/s); "
+        log(f"copy probe: {probe['bytes'] / 1e6:.1f} MB copied in {probe['us']:.2f} us ({probe['GB_s']:.0f} GB/s); "
             f"tq_score at {probe['tq_score_frac_of_probe']:.2f} of it")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -120,6 +120,13 @@ def _load():
     lib.tq_attend_no_alloc.argtypes = [vp, ctypes.POINTER(_CValues), vp, i32, vp, ctypes.c_float, vp,
                                        i32, i32, i32, i32, i32, vp]
     lib.tq_attend_no_alloc.restype = i32
+    sz = ctypes.c_size_t
+    lib.tq_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.tq_probe_read.restype = i32
+    lib.tq_probe_write.argtypes = [vp, sz, vp]
+    lib.tq_probe_write.restype = i32
+    lib.tq_probe_read_write.argtypes = [vp, sz, vp, sz, vp]
+    lib.tq_probe_read_write.restype = i32
     lib.tq_score_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.tq_score_attend_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_score_attend.argtypes = [vp, vp, ctypes.POINTER(_CKeys), vp, i32, ctypes.POINTER(_CValues), vp, i32, vp,

@@ -444,4 +444,45 @@ int tq_decode_debug(const tq_keys* keys, uint8_t* idx_out, int8_t* sign_out, flo
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
+// ---- measurement probes
+namespace {
+constexpr size_t kProbeMaxBytes = (size_t)1 << 36;
+int probe_buffer_ok(const void* p, size_t bytes) {
+    if (bytes % 16 != 0 || bytes > kProbeMaxBytes) return TQ_ERR_ARG;
+    if (bytes > 0 && !p) return TQ_ERR_ARG;
+    if (bytes > 0 && !aligned16(p)) return TQ_ERR_ALIGN;
+    return TQ_OK;
+}
+}  // namespace
+
+int tq_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+    int rc = probe_buffer_ok(src, bytes);
+    if (rc != TQ_OK) return rc;
+    if (bytes == 0) return TQ_OK;
+    if (!sink) return TQ_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_probe_read(src, (int64_t)bytes, static_cast<uint32_t*>(sink),
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_probe_write(void* dst, size_t bytes, void* stream) {
+    int rc = probe_buffer_ok(dst, bytes);
+    if (rc != TQ_OK) return rc;
+    if (bytes == 0) return TQ_OK;
+    const hipError_t e = tq::launch_probe_write(dst, (int64_t)bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_probe_read_write(const void* src, size_t read_bytes, void* dst, size_t write_bytes, void* stream) {
+    int rc = probe_buffer_ok(src, read_bytes);
+    if (rc != TQ_OK) return rc;
+    rc = probe_buffer_ok(dst, write_bytes);
+    if (rc != TQ_OK) return rc;
+    if (read_bytes == 0 || write_bytes == 0) return TQ_ERR_ARG;
+    const hipError_t e = tq::launch_probe_read_write(src, (int64_t)read_bytes, dst, (int64_t)write_bytes,
+                                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -120,6 +120,11 @@ hipError_t launch_score_attend_partial(const float* A, const float* T, KeyStream
 hipError_t launch_attend_combine(const float* ws, const float* Pi_v, float* out, int P, int H, int B, int D, int nch,
                                  hipStream_t stream);
 
+// Streaming probes (probe.hip): bytes must be multiples of 16.
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_probe_write(void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_probe_read_write(const void* src, int64_t rbytes, void* dst, int64_t wbytes, hipStream_t stream);
+
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,
                          int P, int S, int D, hipStream_t stream);

@@ -440,6 +440,29 @@ int tq_score_split(const float* A_hi, const float* A_lo, const tq_split_codes* k
 /* tq_status_string: static description of a status code. */
 const char* tq_status_string(int status);
 
+/*
+ * Measurement probes (not part of the method): kernels that only move bytes,
+ * so a launch of tq_score can be compared with what a launch of the same size
+ * can move on the same GPU. Buffers are device memory, 16-byte aligned; byte
+ * counts are multiples of 16 and at most 2^36. Contents read are arbitrary.
+ *
+ * tq_probe_read: loads every 16-byte word of src once (one word per lane); the
+ *   loaded words are folded into a value that is written to *sink (a 4-byte
+ *   aligned device word) only if it equals an improbable constant.
+ * tq_probe_write: stores every 16-byte word of dst once.
+ * tq_probe_read_write: workgroup k loads its contiguous slice of src (512
+ *   words), then stores its slice of dst (write_bytes spread evenly over the
+ *   workgroups) with values that depend on the words it loaded: the
+ *   codes-in, scores-out dependency of a scoring launch without its arithmetic.
+ *
+ * TQ_ERR_ARG for null pointers with nonzero sizes, sizes that are not
+ * multiples of 16 or exceed 2^36 (and empty read_write calls); TQ_ERR_ALIGN
+ * for misaligned buffers; empty read and write calls return TQ_OK.
+ */
+int tq_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+int tq_probe_write(void* dst, size_t bytes, void* stream);
+int tq_probe_read_write(const void* src, size_t read_bytes, void* dst, size_t write_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,7 @@ EXPECTED = {
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
     "tq_query_transform_hadamard", "tq_score_mse", "tq_query_transform_split", "tq_score_split",
     "tq_score_attend", "tq_score_attend_workspace_bytes", "tq_score_attend_with_mode", "tq_attend_no_alloc",
+    "tq_probe_read", "tq_probe_write", "tq_probe_read_write",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -264,3 +265,20 @@ def test_score_attend_rejects_bad_arguments():
     assert tq._lib.tq_score_attend_workspace_bytes(1, 32, 100, 128, 7) == 0
     g = tq._lib.tq_score_attend_with_mode
     assert g(*a, k, 16, 4, vals(), 16, 4, 16, 1.0, 16, 16, ws, 1, 1, 4, 8, 128, 3, None) == ARG    # unknown form
+
+
+def test_probe_argument_checks_host_only():
+    """The streaming probes validate on the host: no device call for these."""
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib = tq._lib
+    a16, a8 = vp(4096), vp(4104)
+    assert lib.tq_probe_read(None, sz(0), None, None) == OK
+    assert lib.tq_probe_read(None, sz(16), a16, None) == ARG
+    assert lib.tq_probe_read(a16, sz(24), a16, None) == ARG           # not a multiple of 16
+    assert lib.tq_probe_read(a8, sz(16), a16, None) == ALIGN
+    assert lib.tq_probe_read(a16, sz(16), None, None) == ARG          # no sink
+    assert lib.tq_probe_read(a16, sz(1 << 37), a16, None) == ARG      # over 2^36
+    assert lib.tq_probe_write(None, sz(0), None) == OK
+    assert lib.tq_probe_write(a8, sz(32), None) == ALIGN
+    assert lib.tq_probe_read_write(a16, sz(0), a16, sz(16), None) == ARG
+    assert lib.tq_probe_read_write(a16, sz(16), a8, sz(16), None) == ALIGN
