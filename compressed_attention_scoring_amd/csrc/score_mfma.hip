@@ -806,36 +806,49 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     const __amdgpu_buffer_rsrc_t out_r = score_rows(scores + ((int64_t)p * B + (has_q ? b0 : 0)) * S, rows, S);
     float gam_cur = c0.gam;
 
-    // One tile from LDS buffer `buf`. First the next tile's codes `cn` are
-    // unpacked into the other buffer (its gamma kept for the next step) and `cr`
-    // is refilled two tiles ahead; one barrier ends the step.
+    // One tile from LDS buffer `buf`: `cr` is refilled two tiles ahead, this
+    // tile's MFMAs are issued, and then the next tile's codes `cn` are unpacked
+    // into the other buffer (its gamma kept for the next step), so the wait for
+    // those codes comes after this tile's matrix work rather than before it;
+    // one barrier ends the step. Past the last tile `cn` holds a clamped valid
+    // tile whose unpacking nobody reads.
     auto step = [&](int t, uint8_t* buf, uint8_t* other, const TileCodes<NI, NS>& cn, TileCodes<NI, NS>& cr)
         __attribute__((always_inline)) {
-        if (t + stride < ntiles) decode(cn, other);
-        const float gam_next = cn.gam;
         load_tile<LAYOUT, BITS, D, QJL>(cr, idx, sign, gamma,
                                         key0 + min(min(t + 2 * stride, ntiles - 1) * kTileKeys + col, S - 1), g);
         f32x16 accM, accR;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { accM[v] = 0.f; accR[v] = 0.f; }
+        // key operands of k-step j + 1 are read from LDS while the MFMAs of k-step
+        // j run (two register sets in turn), so LDS latency does not stall the chain
         const uint8_t* my = buf + lane * 16;
+        Op8 kop[2][3];
+        auto read_ops = [&](int j, Op8 (&o)[3]) __attribute__((always_inline)) {
+            *reinterpret_cast<uint4*>(o[0].u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 0) * L::BLOCK);
+            *reinterpret_cast<uint4*>(o[1].u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 1) * L::BLOCK);
+            if constexpr (QJL)
+                *reinterpret_cast<uint4*>(o[2].u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 2) * L::BLOCK);
+        };
+        read_ops(0, kop[0]);
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
-            Op8 chi, clo;
-            *reinterpret_cast<uint4*>(chi.u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 0) * L::BLOCK);
-            *reinterpret_cast<uint4*>(clo.u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 1) * L::BLOCK);
-            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, chi.h, accM, 0, 0, 0);
+            const Op8(&o)[3] = kop[j & 1];
+            if (j + 1 < KS) read_ops(j + 1, kop[(j + 1) & 1]);
+            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, o[0].h, accM, 0, 0, 0);
             if constexpr (QJL) {
-                Op8 sg;
-                *reinterpret_cast<uint4*>(sg.u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 2) * L::BLOCK);
-                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, sg.h, accR, 0, 0, 0);
-                accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, chi.h, accM, 0, 0, 0);
-                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[j].h, sg.h, accR, 0, 0, 0);
+                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, o[2].h, accR, 0, 0, 0);
+                accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, o[0].h, accM, 0, 0, 0);
+                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[j].h, o[2].h, accR, 0, 0, 0);
             } else {
-                accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, chi.h, accM, 0, 0, 0);
+                accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, o[0].h, accM, 0, 0, 0);
             }
-            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, clo.h, accM, 0, 0, 0);
+            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, o[1].h, accM, 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QJL ? 3 : 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, QJL ? 5 : 3, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        decode(cn, other);
+        const float gam_next = cn.gam;
         const uint32_t lo = lane_offset(t * kTileKeys + col, S, g);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
