@@ -149,6 +149,38 @@ def test_score_extreme_magnitudes(kernel, B, scale):
     assert np.all(np.abs(got - ref) <= bound)
 
 
+@pytest.mark.parametrize("kernel", ["valu", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
+@pytest.mark.parametrize("B", [3, 32])
+@pytest.mark.parametrize("case", ["tiny", "zero_rows", "tiny_codebook", "zero_codebook"])
+def test_score_tiny_and_zero_operands(kernel, B, case):
+    """Rows and codebooks near the bottom of the fp32 range, and all-zero ones,
+    give finite scores within the tolerance: the power-of-two operand scale is
+    clamped, so it never overflows to inf (inf * 0 would be NaN)."""
+    say(f"score tiny/zero operands kernel={kernel} B={B} case={case}")
+    rng = np.random.default_rng(11)
+    P, S, D, C = 1, 64, 128, 8
+    A = rng.standard_normal((P, B, D)).astype(np.float32)
+    T = (rng.standard_normal((P, B, D)) * 10).astype(np.float32)
+    cb = np.sort(rng.standard_normal(C)).astype(np.float32)
+    if case == "tiny":
+        A *= np.float32(1e-36)
+        T *= np.float32(1e-36)
+    elif case == "zero_rows":
+        A[:, ::2] = 0.0
+        T[:, ::2] = 0.0
+        A[:, 1] *= np.float32(1e-37)
+    elif case == "tiny_codebook":
+        cb *= np.float32(1e-37)
+    else:
+        cb[:] = 0.0
+    idx_u, sign_u, gamma_k, idx, sign = random_codes(rng, P, S, D, C, "packed", 3)
+    got = tq.tq_score_with_kernel(t(A), t(T), keys_to_gpu("packed", 3, idx, sign, gamma_k), t(cb),
+                                  kernel).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = oracle_scores_transformed(A, T, idx_u, sign_u, gamma_k, cb)
+    assert np.all(np.abs(got - ref) <= SCORE_TOL * (1.0 + np.abs(ref)))
+
+
 def test_empty_inputs():
     say("empty inputs")
     D = 128
