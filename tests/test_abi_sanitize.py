@@ -16,7 +16,18 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "compressed_attention_scoring_amd", "csrc")
-SOURCES = ["abi", "query_transform", "score_valu", "score_mfma", "decode", "compress", "attend", "score_split"]
+def _library_sources():
+    """The .hip sources the library build compiles (its SOURCES list)."""
+    import ast
+    with open(os.path.join(ROOT, "compressed_attention_scoring_amd", "build.py")) as f:
+        tree = ast.parse(f.read())
+    for node in tree.body:
+        if isinstance(node, ast.Assign) and any(getattr(t, "id", None) == "SOURCES" for t in node.targets):
+            return [os.path.splitext(s)[0] for s in ast.literal_eval(node.value)]
+    raise AssertionError("build.py has no SOURCES list")
+
+
+SOURCES = _library_sources()
 SANITIZERS = ["address", "undefined"]
 HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/llvm/bin/clang++"
