@@ -53,6 +53,8 @@ MUTATIONS = [
      "return np.asarray(keys, np.float64) @ np.asarray(Pi, np.float64)", COMPRESS_PINS),
     ("compressor signs of S^T r", "oracle/compress.py",
      "proj = r @ np.asarray(S_mat, np.float64).T", "proj = r @ np.asarray(S_mat, np.float64)", COMPRESS_PINS),
+    ("keys compressed without normalising", "oracle/compress.py",
+     "unit = k / np.where(norm > 0.0, norm, 1.0)[:, None]", "unit = k", COMPRESS_PINS),
     ("ties take the upper index", "oracle/compress.py",
      'side="left").astype(np.uint8)', 'side="right").astype(np.uint8)', COMPRESS_PINS),
     ("Gaussian law with variance 2/d", "oracle/codebook.py",
