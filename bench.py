@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     help="decode (default, the quoted configuration); others for profiling")
     ap.add_argument("--kernel", default="auto",
-                    choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared"])
+                    choices=["auto", "valu", "mfma", "mfma_lds", "mfma_reg", "mfma16", "mfma_shared", "mfma_f16"],
+                    help="kernel family of tq_score; mfma_f16 is the single-pass f16 form (2e-2 accuracy)")
     ap.add_argument("--path", default="score", choices=["score", "compress", "attend", "mse", "split", "fused"],
                     help="score (default): the scoring hot path; compress: the key compressor "
                          "(tq_compress_keys) on the workload's key set; attend: softmax and value "
@@ -1138,6 +1139,17 @@ def main() -> int:
         med = rec["per_dispatch_us"]["median"]
         out["roofline"]["trace"] = {"source": rec["profile"], "median_us": med, "avg_us": rec["per_dispatch_us"]["avg"],
                                     "frac_at_median": alg_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    f16_name = tq.tq_score_kernel_name(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, "mfma_f16")
+    if args.kernel == "auto" and mode == "hipgraph" and f16_name is not None:
+        # the single-pass f16 form of the same kernel, reported beside the fp32-accurate one
+        _, _, f16_us = time_phased_graphs(w, ring, shared, "mfma_f16", args.steps)
+        f16_gbs = alg_bytes / (f16_us * 1e-6) / 1e9
+        out["f16_single_pass"] = {
+            "kernel": f16_name, "tq_score_us": f16_us, "achieved_hbm_gbs": f16_gbs,
+            "frac": f16_gbs / HBM_PEAK_GBS, "accuracy": "max |err| / (1 + |exact|) <= 2e-2 (tests/test_gpu_f16.py)",
+            "scores_per_s_score_only": pairs / (f16_us * 1e-6),
+        }
+        log(f"f16 single pass ({f16_name}): {f16_us:.2f} us per tq_score launch ({f16_gbs:.0f} GB/s)")
     if not args.no_stream_probe:
         probes = stream_probes(device, w.key_bytes(), w.score_bytes(), args.steps)
         rw = probes["read_write"]

@@ -55,7 +55,8 @@ TQ_ERR_LAUNCH = -4
 TQ_NO_ALLOC_SCRATCH_BYTES = 48 * 1024 * 1024
 TQ_UNPACKED = 0
 TQ_PACKED = 1
-KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_lds": 3, "mfma_reg": 4, "mfma16": 5, "mfma_shared": 6}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "mfma_lds": 3, "mfma_reg": 4, "mfma16": 5, "mfma_shared": 6,
+           "mfma_f16": 7}   # mfma_f16: single-pass f16, 2e-2 accuracy (tq.h)
 
 
 class _CKeys(ctypes.Structure):

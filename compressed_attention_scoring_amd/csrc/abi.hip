@@ -60,13 +60,14 @@ int mfma_variant(int kernel) {
         case TQ_KERNEL_MFMA_REG: return tq::kMfmaReg;
         case TQ_KERNEL_MFMA16: return tq::kMfmaSmall;
         case TQ_KERNEL_MFMA_SHARED: return tq::kMfmaShared;
+        case TQ_KERNEL_MFMA_F16: return tq::kMfmaF16;
         default: return tq::kMfmaAuto;
     }
 }
 
 bool is_mfma(int kernel) {
     return kernel == TQ_KERNEL_MFMA || kernel == TQ_KERNEL_MFMA_LDS || kernel == TQ_KERNEL_MFMA_REG ||
-           kernel == TQ_KERNEL_MFMA16 || kernel == TQ_KERNEL_MFMA_SHARED;
+           kernel == TQ_KERNEL_MFMA16 || kernel == TQ_KERNEL_MFMA_SHARED || kernel == TQ_KERNEL_MFMA_F16;
 }
 
 bool mfma_ok(int layout, int bits, int C, int B, int S, int D, int kernel = TQ_KERNEL_MFMA) {

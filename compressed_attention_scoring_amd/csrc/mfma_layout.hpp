@@ -11,6 +11,8 @@
 // column l % 32.
 #pragma once
 
+#include <utility>
+
 #include <type_traits>
 
 #include "mfma_ops.hpp"
@@ -384,8 +386,9 @@ struct TileCodes {
 };
 
 // Key-side operands of k-step j: codebook hi and lo parts looked up by index,
-// and signs as f16 +-1.
-template <int LAYOUT, int BITS, int NI, int NS, bool QJL = true>
+// and signs as f16 +-1. LO = false (the single-pass f16 kernels) skips the lo
+// part and leaves `clo` untouched.
+template <int LAYOUT, int BITS, int NI, int NS, bool QJL = true, bool LO = true>
 __device__ __forceinline__ void key_operands(const TileCodes<NI, NS>& c, int j, const uint32_t (&tab_hi)[4],
                                              const uint32_t (&tab_lo)[4], Op8& chi, Op8& clo, Op8& sg) {
     using F = Fmt<LAYOUT, BITS>;
@@ -393,9 +396,65 @@ __device__ __forceinline__ void key_operands(const TileCodes<NI, NS>& c, int j, 
     F::template selectors<NI>(c.iw, j, x0, x1);
     lut4(x0, tab_hi, chi.u[0], chi.u[1]);
     lut4(x1, tab_hi, chi.u[2], chi.u[3]);
-    lut4(x0, tab_lo, clo.u[0], clo.u[1]);
-    lut4(x1, tab_lo, clo.u[2], clo.u[3]);
+    if constexpr (LO) {
+        lut4(x0, tab_lo, clo.u[0], clo.u[1]);
+        lut4(x1, tab_lo, clo.u[2], clo.u[3]);
+    }
     if constexpr (QJL) F::template signs<NS>(c.sw, j, sg.u);
+}
+
+// The tile loop every matrix-core scorer runs. A wavefront (or workgroup) walks
+// tiles tile, tile + stride, ... below ntiles with N code buffers in turn:
+// before tile t is scored from buffer i, the codes of tile t + (N - 1) stride
+// are requested into the buffer tile t - stride used, so each tile's codes are
+// in flight for N - 1 tiles of work. Buffers 0 .. N - 2 hold the first N - 1
+// tiles' requests on entry, and tile < ntiles. `load(Phase<i>, t)` requests
+// tile t's codes into buffer i (any t: the loaders clamp past the end, keeping
+// every load unconditional) and `score(Phase<i>, t)` scores tile t from buffer
+// i. The buffer index is a compile-time constant (the loop is unrolled N
+// times), so a kernel's buffers stay in registers, each in its own array.
+template <int PHASE>
+struct Phase {
+    static constexpr int value = PHASE;
+};
+
+template <int I, int N, typename Load, typename Score>
+__device__ __forceinline__ bool rotate_step(int& tile, int stride, int ntiles, Load& load, Score& score) {
+    load(Phase<(I + N - 1) % N>{}, tile + (N - 1) * stride);
+    score(Phase<I>{}, tile);
+    tile += stride;
+    return tile >= ntiles;
+}
+
+template <int N, typename Load, typename Score, int... I>
+__device__ __forceinline__ bool rotate_round(int& tile, int stride, int ntiles, Load& load, Score& score,
+                                             std::integer_sequence<int, I...>) {
+    bool done = false;
+    ((done = done || rotate_step<I, N>(tile, stride, ntiles, load, score)), ...);
+    return done;
+}
+
+template <int N, typename Load, typename Score>
+__device__ __forceinline__ void rotate_tiles(int tile, int stride, int ntiles, Load&& load, Score&& score) {
+    while (!rotate_round<N>(tile, stride, ntiles, load, score, std::make_integer_sequence<int, N>{})) {
+    }
+}
+
+// The same walk over an array of N code buffers: load(codes, t), score(codes, t).
+template <int N, typename Codes, typename Load, typename Score>
+__device__ __forceinline__ void rotate_tiles(Codes (&buf)[N], int tile, int stride, int ntiles, Load&& load,
+                                             Score&& score) {
+    rotate_tiles<N>(
+        tile, stride, ntiles,
+        [&](auto ph, int t) __attribute__((always_inline)) { load(buf[decltype(ph)::value], t); },
+        [&](auto ph, int t) __attribute__((always_inline)) { score(buf[decltype(ph)::value], t); });
+}
+
+// A step that owns its loads and alternates two phases (LDS buffers):
+// step(Phase<0>, t), step(Phase<1>, t), ...
+template <typename Step>
+__device__ __forceinline__ void alternate_tiles(int tile, int stride, int ntiles, Step&& step) {
+    rotate_tiles<2>(tile, stride, ntiles, [](auto, int) __attribute__((always_inline)) {}, step);
 }
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
@@ -442,7 +501,8 @@ __device__ __forceinline__ int slot_pos(int p, int j) {
 // (whole_block_slots, packed_sign_pairs); the 3-bit codebook operand keeps
 // 2-byte stores. `live` is false for rows past the tile: such lanes still take
 // part in the sign exchange with their neighbour but store nothing.
-template <int LAYOUT, int BITS, bool QJL, int SEG>
+// LO = false (the single-pass f16 kernels) stores the hi parts only.
+template <int LAYOUT, int BITS, bool QJL, int SEG, bool LO = true>
 __device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int blk16, const float (&a)[SEG],
                                                const float (&t)[SEG], float sA, float sT, bool live) {
     static_assert(SEG == 16, "blocks of 16 coordinates");
@@ -458,7 +518,7 @@ __device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int bl
                 const int j = 2 * blk16 + sl;
                 uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16;
                 *reinterpret_cast<uint4*>(base + 0 * BLOCK) = whole_slot<LAYOUT, BITS, true>(ah, sl);
-                *reinterpret_cast<uint4*>(base + 1 * BLOCK) = whole_slot<LAYOUT, BITS, true>(al, sl);
+                if constexpr (LO) *reinterpret_cast<uint4*>(base + 1 * BLOCK) = whole_slot<LAYOUT, BITS, true>(al, sl);
             }
         }
     } else if (live) {
@@ -468,7 +528,7 @@ __device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int bl
             mse_slot16<LAYOUT, BITS>(blk16, k, j, e);
             uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16 + e * 2;
             *reinterpret_cast<uint16_t*>(base + 0 * BLOCK) = ah[k];
-            *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = al[k];
+            if constexpr (LO) *reinterpret_cast<uint16_t*>(base + 1 * BLOCK) = al[k];
         }
     }
     if constexpr (QJL) {
@@ -482,7 +542,8 @@ __device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int bl
                     const int j = 2 * blk16 + sl;
                     uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16;
                     *reinterpret_cast<uint4*>(base + 2 * BLOCK) = whole_slot<LAYOUT, BITS, false>(th, sl);
-                    *reinterpret_cast<uint4*>(base + 3 * BLOCK) = whole_slot<LAYOUT, BITS, false>(tl, sl);
+                    if constexpr (LO)
+                        *reinterpret_cast<uint4*>(base + 3 * BLOCK) = whole_slot<LAYOUT, BITS, false>(tl, sl);
                 }
             }
         } else {
@@ -511,7 +572,7 @@ __device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int bl
                     mine_h[w] = odd ? own_h[2 + cc][w] : own_h[cc][w];
                     mine_l[w] = odd ? own_l[2 + cc][w] : own_l[cc][w];
                     got_h[w] = (uint32_t)__shfl_xor((int)send_h, 1);
-                    got_l[w] = (uint32_t)__shfl_xor((int)send_l, 1);
+                    got_l[w] = LO ? (uint32_t)__shfl_xor((int)send_l, 1) : 0u;
                 }
                 // element 2 i + parity: the even lane's value, then the odd lane's
                 uint32_t oh[4], ol[4];
@@ -528,7 +589,8 @@ __device__ __forceinline__ void prologue_store(uint8_t* tile_base, int p, int bl
                     const int j = 4 * (blk16 >> 1) + 2 * (blk16 & 1) + cc;
                     uint8_t* base = tile_base + (j * 4) * BLOCK + slot_pos(p, j) * 16;
                     *reinterpret_cast<uint4*>(base + 2 * BLOCK) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
-                    *reinterpret_cast<uint4*>(base + 3 * BLOCK) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+                    if constexpr (LO)
+                        *reinterpret_cast<uint4*>(base + 3 * BLOCK) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
                 }
             }
         }

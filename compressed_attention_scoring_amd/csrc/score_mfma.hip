@@ -52,7 +52,10 @@ using namespace layout;
 
 
 // QJL = false scores MSE-only keys: scores = norm_s * M (no T, no signs).
-template <int LAYOUT, int BITS, int D, int MT, bool QJL>
+// F16 = true is the single-pass f16 form (with QJL): one product per
+// contraction, A_hi c_hi into M and T_hi sigma into R, so the lo halves are
+// neither stored nor read nor looked up.
+template <int LAYOUT, int BITS, int D, int MT, bool QJL, bool F16 = false>
 __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
@@ -86,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
 
     int tile = blockIdx.x * kWaves + wave;
     const int stride = gridDim.x * kWaves;
-    TileCodes<NI, NS> cur;
+    TileCodes<NI, NS> codes[2];               // code buffers of the tile loop
+    TileCodes<NI, NS>& cur = codes[0];
 
     // codebook byte tables for v_perm lookups and its scale, filled in the
     // prologue once A, T and the first tile's codes have been requested
@@ -154,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         const int d0 = pl * SEG;
         const int gg = d0 / HALF;                               // lane segment holding these coordinates
         const int blk16 = (d0 % HALF) / SEG;                    // their 16-coordinate block in it
-        prologue_store<LAYOUT, BITS, QJL, SEG>(ops + (mtile * KS * 4) * BLOCK, gg * 32 + rl, blk16, a, t, sA, sT,
-                                               row < MT * 32);
+        prologue_store<LAYOUT, BITS, QJL, SEG, !F16>(ops + (mtile * KS * 4) * BLOCK, gg * 32 + rl, blk16, a, t, sA,
+                                                     sT, row < MT * 32);
     }
     __syncthreads();
 
@@ -172,9 +176,10 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             for (int v = 0; v < 16; ++v) { accM[mt][v] = 0.f; accR[mt][v] = 0.f; }
         }
         Op8 chi[2], clo[2], sg[2];
-        key_operands<LAYOUT, BITS, NI, NS, QJL>(c, 0, tab_hi, tab_lo, chi[0], clo[0], sg[0]);
-        constexpr int NOPS = QJL ? 4 : 2;      // LDS operand blocks read per 32-query tile and k-step
-        constexpr int NMFMA = QJL ? 5 : 3;     // products per 32-query tile and k-step
+        key_operands<LAYOUT, BITS, NI, NS, QJL, !F16>(c, 0, tab_hi, tab_lo, chi[0], clo[0], sg[0]);
+        // LDS operand blocks read and products per 32-query tile and k-step
+        constexpr int NOPS = F16 ? 2 : QJL ? 4 : 2;
+        constexpr int NMFMA = F16 ? 2 : QJL ? 5 : 3;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             const int u = j & 1;
@@ -183,23 +188,28 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
             for (int mt = 0; mt < MT; ++mt) {
                 const uint8_t* base = ops + ((mt * KS + j) * 4) * BLOCK + slot_pos(lane, j) * 16;
                 *reinterpret_cast<uint4*>(ahi[mt].u) = *reinterpret_cast<const uint4*>(base + 0 * BLOCK);
-                *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
+                if constexpr (!F16)
+                    *reinterpret_cast<uint4*>(alo[mt].u) = *reinterpret_cast<const uint4*>(base + 1 * BLOCK);
                 if constexpr (QJL) {
                     *reinterpret_cast<uint4*>(thi[mt].u) = *reinterpret_cast<const uint4*>(base + 2 * BLOCK);
-                    *reinterpret_cast<uint4*>(tlo[mt].u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
+                    if constexpr (!F16)
+                        *reinterpret_cast<uint4*>(tlo[mt].u) = *reinterpret_cast<const uint4*>(base + 3 * BLOCK);
                 }
             }
             if (j + 1 < KS)
-                key_operands<LAYOUT, BITS, NI, NS, QJL>(c, j + 1, tab_hi, tab_lo, chi[u ^ 1], clo[u ^ 1], sg[u ^ 1]);
+                key_operands<LAYOUT, BITS, NI, NS, QJL, !F16>(c, j + 1, tab_hi, tab_lo, chi[u ^ 1], clo[u ^ 1],
+                                                             sg[u ^ 1]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, chi[u].h, accM[mt], 0, 0, 0);
                 if constexpr (QJL)
                     accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[mt].h, sg[u].h, accR[mt], 0, 0, 0);
-                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[mt].h, chi[u].h, accM[mt], 0, 0, 0);
-                if constexpr (QJL)
-                    accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[mt].h, sg[u].h, accR[mt], 0, 0, 0);
-                accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, clo[u].h, accM[mt], 0, 0, 0);
+                if constexpr (!F16) {
+                    accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[mt].h, chi[u].h, accM[mt], 0, 0, 0);
+                    if constexpr (QJL)
+                        accR[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[mt].h, sg[u].h, accR[mt], 0, 0, 0);
+                    accM[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[mt].h, clo[u].h, accM[mt], 0, 0, 0);
+                }
             }
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NOPS * MT, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
@@ -226,22 +236,16 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         }
     };
 
-    // Two code buffers in turn, as in score_qs_kernel. Wavefronts without a tile
-    // took part in the prologue (it ends in a barrier) and leave here.
+    // Two code buffers in turn. Wavefronts without a tile took part in the
+    // prologue (it ends in a barrier) and leave here.
     if (tile < ntiles) {
-        TileCodes<NI, NS> nxt;
-        while (true) {
-            load_tile<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
-                                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
-            tile_scores(cur, tile);
-            tile += stride;
-            if (tile >= ntiles) break;
-            load_tile<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma,
-                                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
-            tile_scores(nxt, tile);
-            tile += stride;
-            if (tile >= ntiles) break;
-        }
+        rotate_tiles<2>(
+            codes, tile, stride, ntiles,
+            [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
+                load_tile<LAYOUT, BITS, D, QJL>(c, idx, sign, gamma,
+                                                key0 + min(min(t, ntiles - 1) * kTileKeys + col, S - 1), g);
+            },
+            tile_scores);
     }
 }
 
@@ -326,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
     int tile = blockIdx.x * kWaves + wave;
     const int stride = gridDim.x * kWaves;
 
-    SplitTileCodes cur;
+    SplitTileCodes codes[2];                   // code buffers of the tile loop
+    SplitTileCodes& cur = codes[0];
     float sch = 1.f, scl = 1.f;
     uint32_t th_hi[4], th_lo[4], tl_hi[4], tl_lo[4];
 
@@ -475,19 +480,13 @@ __global__ __launch_bounds__(kThreads) void score_split_mfma_kernel(
     };
 
     if (tile < ntiles) {
-        SplitTileCodes nxt;
-        while (true) {
-            load_split_tile(nxt, idx_hi, norm_hi, idx_lo, norm_lo,
-                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
-            tile_scores(cur, tile);
-            tile += stride;
-            if (tile >= ntiles) break;
-            load_split_tile(cur, idx_hi, norm_hi, idx_lo, norm_lo,
-                            key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
-            tile_scores(nxt, tile);
-            tile += stride;
-            if (tile >= ntiles) break;
-        }
+        rotate_tiles<2>(
+            codes, tile, stride, ntiles,
+            [&](SplitTileCodes& c, int t) __attribute__((always_inline)) {
+                load_split_tile(c, idx_hi, norm_hi, idx_lo, norm_lo,
+                                key0 + min(min(t, ntiles - 1) * kTileKeys + col, S - 1), g);
+            },
+            tile_scores);
     }
 }
 
@@ -550,7 +549,8 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
     }
     // first tile's codes right behind A and T (see score_mfma_kernel for why the
     // loads are unconditional and fenced)
-    TileCodes<NI, NS> cur;
+    TileCodes<NI, NS> codes[2];               // code buffers of the tile loop
+    TileCodes<NI, NS>& cur = codes[0];
     asm volatile("" ::: "memory");
     {
         const int s = min(tile * kTileKeys + col, S - 1);
@@ -647,23 +647,12 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
     // for one buffer never waits for the other's loads); the next tile's codes
     // are requested before the current tile is computed, clamped and
     // unconditional like the first load.
-    TileCodes<NI, NS> nxt;
-    while (true) {
-        {
-            const int s = min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1);
-            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma, key0 + s, g);
-        }
-        tile_scores(cur, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-        {
-            const int s = min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1);
-            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
-        }
-        tile_scores(nxt, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-    }
+    rotate_tiles<2>(
+        codes, tile, stride, ntiles,
+        [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
+            load_tile<LAYOUT, BITS, D>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys + col, S - 1), g);
+        },
+        tile_scores);
 }
 
 // ---------------------------------------------------------------------------
@@ -675,49 +664,56 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
 // workgroup barrier per tile. This removes the fourfold key decoding of the
 // register variant, whose main loop was bound by vector-ALU issue.
 // ---------------------------------------------------------------------------
-template <int LAYOUT, int BITS, int D, bool QJL = true>
+// Per k-step LDS blocks: the codebook's hi part, its lo part unless F16, and
+// the signs with QJL.
+template <int LAYOUT, int BITS, int D, bool QJL = true, bool F16 = false>
 struct SharedLds {
     static constexpr int KS = D / 16;
     static constexpr int BLOCK = 64 * 16;                       // one operand: 64 lanes x 16 bytes
-    static constexpr int NB = QJL ? 3 : 2;                      // operands per k-step
-    static constexpr int BUF = KS * NB * BLOCK;                 // chi, clo (and sg) of every k-step
+    static constexpr int CLO = 1;                               // block of the codebook lo part (not F16)
+    static constexpr int SG = F16 ? 1 : 2;                      // block of the signs (QJL)
+    static constexpr int NB = (F16 ? 1 : 2) + (QJL ? 1 : 0);    // operands per k-step
+    static constexpr int BUF = KS * NB * BLOCK;
 };
 
-template <int LAYOUT, int BITS, int D, int W, bool QJL = true>
+template <int LAYOUT, int BITS, int D, int W, bool QJL = true, bool F16 = false>
 __device__ __forceinline__ void decode_share(const TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
                                                          Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
                                              const uint32_t (&tab_hi)[4], const uint32_t (&tab_lo)[4],
                                              uint8_t* buf, int lane) {
     using F = Fmt<LAYOUT, BITS>;
     constexpr int NI = F::template idx_dw<D>(), NS = F::template sign_dw<D>();
-    using L = SharedLds<LAYOUT, BITS, D, QJL>;
+    using L = SharedLds<LAYOUT, BITS, D, QJL, F16>;
     constexpr int KS = D / 16, JW = KS / kWaves, BLOCK = L::BLOCK;
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
         const int j = W * JW + jj;
         Op8 chi, clo, sg;
-        key_operands<LAYOUT, BITS, NI, NS, QJL>(c, j, tab_hi, tab_lo, chi, clo, sg);
+        key_operands<LAYOUT, BITS, NI, NS, QJL, !F16>(c, j, tab_hi, tab_lo, chi, clo, sg);
         uint8_t* base = buf + (j * L::NB) * BLOCK + lane * 16;
         *reinterpret_cast<uint4*>(base + 0 * BLOCK) = *reinterpret_cast<const uint4*>(chi.u);
-        *reinterpret_cast<uint4*>(base + 1 * BLOCK) = *reinterpret_cast<const uint4*>(clo.u);
-        if constexpr (QJL) *reinterpret_cast<uint4*>(base + 2 * BLOCK) = *reinterpret_cast<const uint4*>(sg.u);
+        if constexpr (!F16) *reinterpret_cast<uint4*>(base + L::CLO * BLOCK) = *reinterpret_cast<const uint4*>(clo.u);
+        if constexpr (QJL) *reinterpret_cast<uint4*>(base + L::SG * BLOCK) = *reinterpret_cast<const uint4*>(sg.u);
     }
 }
 
 // QJL = false: MSE-only keys (no sign stream, no T, gamma = the key's norm).
-template <int LAYOUT, int BITS, int D, bool QJL = true>
+// F16 = true (with QJL): the single-pass f16 form, two products per k-step
+// (A_hi c_hi, T_hi sigma) and no lo halves in registers or LDS.
+template <int LAYOUT, int BITS, int D, bool QJL = true, bool F16 = false>
 __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
     const void* __restrict__ gamma, const float* __restrict__ codebook, int C,
     float* __restrict__ scores, int B, int S, float coef) {
     using F = Fmt<LAYOUT, BITS>;
-    using L = SharedLds<LAYOUT, BITS, D, QJL>;
+    using L = SharedLds<LAYOUT, BITS, D, QJL, F16>;
     constexpr int HALF = D / 2;
     constexpr int KS = D / 16;
     constexpr int NI = F::template idx_dw<D>();
     constexpr int NS = F::template sign_dw<D>();
     constexpr int QT = QJL ? KS : 1;            // T operands kept (none without QJL)
+    constexpr int LT = F16 ? 1 : KS;            // lo halves kept (none in the f16 form)
     static_assert(KS % kWaves == 0, "each wavefront unpacks the same number of k-steps");
 
     __shared__ __attribute__((aligned(16))) uint8_t kops[2 * L::BUF];
@@ -772,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     const float sA = pow2_scale_for(ma);
     const float sT = pow2_scale_for(mt);
     if (g == 0) rowk[wave][col] = make_float2(inv_scales(sA, sc), coef / sT);
-    Op8 ahi[KS], alo[KS], thi[QT], tlo[QT];
+    Op8 ahi[KS], alo[LT], thi[QT], tlo[F16 ? 1 : QT];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
 #pragma unroll
@@ -780,22 +776,22 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
             const float xa = a[mse_dim<LAYOUT, BITS>(j, e)] * sA;
             const _Float16 ha = (_Float16)xa;
             ahi[j].h[e] = ha;
-            alo[j].h[e] = (_Float16)(xa - (float)ha);
+            if constexpr (!F16) alo[j].h[e] = (_Float16)(xa - (float)ha);
             if constexpr (QJL) {
                 const float xt = t[qjl_dim<LAYOUT>(j, e)] * sT;
                 const _Float16 ht = (_Float16)xt;
                 thi[j].h[e] = ht;
-                tlo[j].h[e] = (_Float16)(xt - (float)ht);
+                if constexpr (!F16) tlo[j].h[e] = (_Float16)(xt - (float)ht);
             }
         }
     }
 
     auto decode = [&](const TileCodes<NI, NS>& c, uint8_t* buf) __attribute__((always_inline)) {
         switch (wave) {
-            case 0: decode_share<LAYOUT, BITS, D, 0, QJL>(c, tab_hi, tab_lo, buf, lane); break;
-            case 1: decode_share<LAYOUT, BITS, D, 1, QJL>(c, tab_hi, tab_lo, buf, lane); break;
-            case 2: decode_share<LAYOUT, BITS, D, 2, QJL>(c, tab_hi, tab_lo, buf, lane); break;
-            default: decode_share<LAYOUT, BITS, D, 3, QJL>(c, tab_hi, tab_lo, buf, lane); break;
+            case 0: decode_share<LAYOUT, BITS, D, 0, QJL, F16>(c, tab_hi, tab_lo, buf, lane); break;
+            case 1: decode_share<LAYOUT, BITS, D, 1, QJL, F16>(c, tab_hi, tab_lo, buf, lane); break;
+            case 2: decode_share<LAYOUT, BITS, D, 2, QJL, F16>(c, tab_hi, tab_lo, buf, lane); break;
+            default: decode_share<LAYOUT, BITS, D, 3, QJL, F16>(c, tab_hi, tab_lo, buf, lane); break;
         }
     };
     decode(c0, kops);
@@ -823,11 +819,15 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
         // j run (two register sets in turn), so LDS latency does not stall the chain
         const uint8_t* my = buf + lane * 16;
         Op8 kop[2][3];
+        // o[0]: codebook hi, o[1]: codebook lo (not F16), o[2]: signs (QJL)
         auto read_ops = [&](int j, Op8 (&o)[3]) __attribute__((always_inline)) {
             *reinterpret_cast<uint4*>(o[0].u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 0) * L::BLOCK);
-            *reinterpret_cast<uint4*>(o[1].u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 1) * L::BLOCK);
+            if constexpr (!F16)
+                *reinterpret_cast<uint4*>(o[1].u) =
+                    *reinterpret_cast<const uint4*>(my + (j * L::NB + L::CLO) * L::BLOCK);
             if constexpr (QJL)
-                *reinterpret_cast<uint4*>(o[2].u) = *reinterpret_cast<const uint4*>(my + (j * L::NB + 2) * L::BLOCK);
+                *reinterpret_cast<uint4*>(o[2].u) =
+                    *reinterpret_cast<const uint4*>(my + (j * L::NB + L::SG) * L::BLOCK);
         };
         read_ops(0, kop[0]);
 #pragma unroll
@@ -835,16 +835,18 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
             const Op8(&o)[3] = kop[j & 1];
             if (j + 1 < KS) read_ops(j + 1, kop[(j + 1) & 1]);
             accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, o[0].h, accM, 0, 0, 0);
-            if constexpr (QJL) {
+            if constexpr (F16) {
+                accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, o[2].h, accR, 0, 0, 0);
+            } else if constexpr (QJL) {
                 accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(thi[j].h, o[2].h, accR, 0, 0, 0);
                 accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, o[0].h, accM, 0, 0, 0);
                 accR = __builtin_amdgcn_mfma_f32_32x32x16_f16(tlo[j].h, o[2].h, accR, 0, 0, 0);
             } else {
                 accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[j].h, o[0].h, accM, 0, 0, 0);
             }
-            accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, o[1].h, accM, 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QJL ? 3 : 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, QJL ? 5 : 3, 0);
+            if constexpr (!F16) accM = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[j].h, o[1].h, accM, 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, L::NB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, F16 ? 2 : QJL ? 5 : 3, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         decode(cn, other);
@@ -861,14 +863,12 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
         gam_cur = gam_next;
         __syncthreads();
     };
-    while (true) {
-        step(tile, kops, kops + L::BUF, c1, c0);
-        tile += stride;
-        if (tile >= ntiles) break;
-        step(tile, kops + L::BUF, kops, c0, c1);
-        tile += stride;
-        if (tile >= ntiles) break;
-    }
+    alternate_tiles(tile, stride, ntiles, [&](auto phase, int t) __attribute__((always_inline)) {
+        if constexpr (decltype(phase)::value == 0)
+            step(t, kops, kops + L::BUF, c1, c0);
+        else
+            step(t, kops + L::BUF, kops, c0, c1);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -918,7 +918,10 @@ __device__ __forceinline__ void load_quarter(TileCodes<SmallFmt<LAYOUT, BITS, D>
 // types 0 and 1 stay A_hi and A_lo against the codebook's hi part in elements
 // 0-3, type 2 is A_hi against its lo part in elements 4-7, type 3 is zero, so
 // two MFMAs per k-step cover what takes three with signs.
-template <int LAYOUT, int BITS, int D, int MINW, bool QJL = true>
+// F16 = true (with QJL): the codebook enters as its f16 hi part only (no lo
+// lookups, no third MFMA); the query's lo rows ride in the same two
+// instructions as its hi rows, so they are kept.
+template <int LAYOUT, int BITS, int D, int MINW, bool QJL = true, bool F16 = false>
 __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
@@ -952,7 +955,8 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
         const float4 v = *reinterpret_cast<const float4*>(src + k);
         x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
     }
-    TileCodes<NI, NS> cur;
+    TileCodes<NI, NS> codes[3];               // code buffers of the tile loop
+    TileCodes<NI, NS>& cur = codes[0];
     asm volatile("" ::: "memory");
     load_quarter<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
     asm volatile("" ::: "memory");
@@ -978,7 +982,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     // (coordinates mse_dim(j, 0..3) and (j, 4..7)) with sign elements 4-7
     // (coordinates qjl_dim(j, 0..3) and (j, 4..7)); ops[j][2] is A_hi over
     // mse_dim(j, 0..7) for the codebook-lo product.
-    constexpr int NO = QJL ? 3 : 2;
+    constexpr int NO = QJL && !F16 ? 3 : 2;
     Op8 ops[NJ][NO];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -1000,7 +1004,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
                 }
             }
         }
-        if constexpr (QJL) {
+        if constexpr (QJL && !F16) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xa = x[mse_dim<LAYOUT, BITS>(j, e)] * s_row;
@@ -1026,11 +1030,14 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
                 Op8 kl;
                 k0.u[2] = sgn[0]; k0.u[3] = sgn[1];
                 k1.u[2] = sgn[2]; k1.u[3] = sgn[3];
-                lut4(x0, tab_lo, kl.u[0], kl.u[1]);
-                lut4(x1, tab_lo, kl.u[2], kl.u[3]);
+                if constexpr (!F16) {
+                    lut4(x0, tab_lo, kl.u[0], kl.u[1]);
+                    lut4(x1, tab_lo, kl.u[2], kl.u[3]);
+                }
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][0].h, k0.h, acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][1].h, k1.h, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][2].h, kl.h, acc, 0, 0, 0);
+                if constexpr (!F16)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ops[j][NO - 1].h, kl.h, acc, 0, 0, 0);
             } else {
                 lut4(x0, tab_lo, k0.u[2], k0.u[3]);
                 lut4(x1, tab_lo, k1.u[2], k1.u[3]);
@@ -1048,29 +1055,12 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
     };
 
     // three code buffers in turn: each tile's codes are requested two tiles ahead
-    TileCodes<NI, NS> nxt, nx2;
-    load_quarter<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
-                                       key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1), gq);
-    while (true) {
-        load_quarter<LAYOUT, BITS, D, QJL>(nx2, idx, sign, gamma,
-                                           key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1),
+    auto load = [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
+        load_quarter<LAYOUT, BITS, D, QJL>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys16 + kc, S - 1),
                                            gq);
-        tile_scores(cur, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-        load_quarter<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma,
-                                           key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1),
-                                           gq);
-        tile_scores(nxt, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-        load_quarter<LAYOUT, BITS, D, QJL>(nxt, idx, sign, gamma,
-                                           key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1),
-                                           gq);
-        tile_scores(nx2, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-    }
+    };
+    load(codes[1], tile + stride);
+    rotate_tiles<3>(codes, tile, stride, ntiles, load, tile_scores);
 }
 
 // ---------------------------------------------------------------------------
@@ -1146,7 +1136,8 @@ __global__ __launch_bounds__(kThreads, MINW) void score_split16_kernel(
         const float4 v = *reinterpret_cast<const float4*>(src + k);
         x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
     }
-    Codes cur;
+    Codes codes[3];                            // code buffers of the tile loop
+    Codes& cur = codes[0];
     asm volatile("" ::: "memory");
     load(cur, key0 + min(tile * kTileKeys16 + kc, S - 1));
     asm volatile("" ::: "memory");
@@ -1216,22 +1207,11 @@ __global__ __launch_bounds__(kThreads, MINW) void score_split16_kernel(
     };
 
     // three code buffers in turn: each tile's codes are requested two tiles ahead
-    Codes nxt, nx2;
-    load(nxt, key0 + min(min(tile + stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
-    while (true) {
-        load(nx2, key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
-        tile_scores(cur, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-        load(cur, key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
-        tile_scores(nxt, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-        load(nxt, key0 + min(min(tile + 2 * stride, ntiles - 1) * kTileKeys16 + kc, S - 1));
-        tile_scores(nx2, tile);
-        tile += stride;
-        if (tile >= ntiles) break;
-    }
+    auto load_tile_codes = [&](Codes& c, int t) __attribute__((always_inline)) {
+        load(c, key0 + min(min(t, ntiles - 1) * kTileKeys16 + kc, S - 1));
+    };
+    load_tile_codes(codes[1], tile + stride);
+    rotate_tiles<3>(codes, tile, stride, ntiles, load_tile_codes, tile_scores);
 }
 
 // ---------------------------------------------------------------------------
@@ -1313,7 +1293,8 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
 
     float sc = 1.f;
     uint32_t tab_hi[4] = {0u, 0u, 0u, 0u}, tab_lo[4] = {0u, 0u, 0u, 0u};
-    TileCodes<NI, NS> cur;
+    TileCodes<NI, NS> codes[2];                  // key code buffers of the tile loop
+    TileCodes<NI, NS>& cur = codes[0];
     int tl = wave;                                 // this wavefront's tiles: wave, wave + 4, ...
     auto tile_key = [&](int t) { return min(s_begin + min(t, ntl - 1) * kTileKeys + col, S - 1); };
 
@@ -1532,21 +1513,17 @@ __global__ __launch_bounds__(kThreads) void score_attend_kernel(
     };
 
     if (tl < ntl) {
-        TileCodes<NI, NS> nxt;
-        VRaw va, vb;
-        load_values(va, tl);
-        while (true) {
-            load_tile<LAYOUT, BITS, D>(nxt, idx, sign, gamma, key0 + tile_key(tl + kWaves), g);
-            load_values(vb, tl + kWaves);
-            tile_attend(cur, va, tl);
-            tl += kWaves;
-            if (tl >= ntl) break;
-            load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + tile_key(tl + kWaves), g);
-            load_values(va, tl + kWaves);
-            tile_attend(nxt, vb, tl);
-            tl += kWaves;
-            if (tl >= ntl) break;
-        }
+        VRaw vals[2];                                // the raw values travel with the key codes
+        load_values(vals[0], tl);
+        rotate_tiles<2>(
+            tl, kWaves, ntl,
+            [&](auto ph, int t) __attribute__((always_inline)) {
+                load_tile<LAYOUT, BITS, D>(codes[decltype(ph)::value], idx, sign, gamma, key0 + tile_key(t), g);
+                load_values(vals[decltype(ph)::value], t);
+            },
+            [&](auto ph, int t) __attribute__((always_inline)) {
+                tile_attend(codes[decltype(ph)::value], vals[decltype(ph)::value], t);
+            });
     }
 
     // ---- this wavefront's (m, l, acc) to LDS (true scale), then merge the four
@@ -1600,7 +1577,7 @@ int mt_for(int B, int D) {
     return 1;
 }
 
-template <int LAYOUT, int BITS, int D, int MT, bool QJL>
+template <int LAYOUT, int BITS, int D, int MT, bool QJL, bool F16 = false>
 hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                      float* scores, int P, int B, int S, hipStream_t stream) {
     const int groups_y = (B + MT * 32 - 1) / (MT * 32);
@@ -1619,7 +1596,7 @@ hipError_t launch_mt(const float* A, const float* T, KeyStreams k, const float* 
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT, QJL>), dim3((unsigned)gx, groups_y, P),
+    hipLaunchKernelGGL((score_mfma_kernel<LAYOUT, BITS, D, MT, QJL, F16>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();
@@ -1676,7 +1653,7 @@ hipError_t launch_qs_d(const float* A, const float* T, KeyStreams k, const float
 // Small-batch launch: workgroup rows are groups of four queries; MINW
 // wavefronts per SIMD are resident (the kernel needs about 105 registers at
 // D = 128 with signs), so 256 * MINW workgroups fill the chip.
-template <int LAYOUT, int BITS, int D, bool QJL = true>
+template <int LAYOUT, int BITS, int D, bool QJL = true, bool F16 = false>
 hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                           float* scores, int P, int B, int S, hipStream_t stream) {
     // without signs the kernel needs about 72 registers at D = 128: six wavefronts per SIMD
@@ -1688,23 +1665,23 @@ hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const fl
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_mfma16_kernel<LAYOUT, BITS, D, MINW, QJL>), dim3((unsigned)gx, groups_y, P),
+    hipLaunchKernelGGL((score_mfma16_kernel<LAYOUT, BITS, D, MINW, QJL, F16>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();
 }
 
-template <int LAYOUT, int BITS, bool QJL = true>
+template <int LAYOUT, int BITS, bool QJL = true, bool F16 = false>
 hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                                int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
-    if (D == 128) return launch_small_d<LAYOUT, BITS, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (D == 256) return launch_small_d<LAYOUT, BITS, 256, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 128) return launch_small_d<LAYOUT, BITS, 128, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 256) return launch_small_d<LAYOUT, BITS, 256, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     return hipErrorInvalidValue;
 }
 
 // Shared-decode launch: workgroup rows are groups of four 32-query tiles; two
 // workgroups per CU are resident (registers), so 512 workgroups fill the chip.
-template <int LAYOUT, int BITS, int D, bool QJL = true>
+template <int LAYOUT, int BITS, int D, bool QJL = true, bool F16 = false>
 hipError_t launch_shared_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                            float* scores, int P, int B, int S, hipStream_t stream) {
     const int groups_y = (B + 127) / 128;
@@ -1714,17 +1691,17 @@ hipError_t launch_shared_d(const float* A, const float* T, KeyStreams k, const f
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_shared_kernel<LAYOUT, BITS, D, QJL>), dim3((unsigned)gx, groups_y, P),
+    hipLaunchKernelGGL((score_shared_kernel<LAYOUT, BITS, D, QJL, F16>), dim3((unsigned)gx, groups_y, P),
                        dim3(kThreads), 0, stream, A, T, k.idx, k.sign, k.gamma, codebook, C,
                        scores, B, S, coef);
     return hipGetLastError();
 }
 
-template <int LAYOUT, int BITS, bool QJL = true>
+template <int LAYOUT, int BITS, bool QJL = true, bool F16 = false>
 hipError_t launch_shared_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                                 int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
-    if (D == 64) return launch_shared_d<LAYOUT, BITS, 64, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (D == 128) return launch_shared_d<LAYOUT, BITS, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 64) return launch_shared_d<LAYOUT, BITS, 64, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (D == 128) return launch_shared_d<LAYOUT, BITS, 128, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     return hipErrorInvalidValue;
 }
 
@@ -1743,32 +1720,32 @@ hipError_t launch_qs_layout(const float* A, const float* T, KeyStreams k, const 
     return hipErrorInvalidValue;
 }
 
-template <int LAYOUT, int BITS, int D, bool QJL>
+template <int LAYOUT, int BITS, int D, bool QJL, bool F16 = false>
 hipError_t launch_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
                     float* scores, int P, int B, int S, hipStream_t stream) {
     switch (mt_for(B, D)) {
         case 4:
             if constexpr (D <= 128)
-                return launch_mt<LAYOUT, BITS, D, 4, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+                return launch_mt<LAYOUT, BITS, D, 4, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
             [[fallthrough]];
         case 2:
-            return launch_mt<LAYOUT, BITS, D, 2, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+            return launch_mt<LAYOUT, BITS, D, 2, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
         default:
-            return launch_mt<LAYOUT, BITS, D, 1, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+            return launch_mt<LAYOUT, BITS, D, 1, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     }
 }
 
-template <int LAYOUT, int BITS, bool QJL = true>
+template <int LAYOUT, int BITS, bool QJL = true, bool F16 = false>
 hipError_t launch_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                          int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
     switch (D) {
         case 32:
             if constexpr (LAYOUT == 0)
-                return launch_d<LAYOUT, BITS, 32, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+                return launch_d<LAYOUT, BITS, 32, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
             break;
-        case 64: return launch_d<LAYOUT, BITS, 64, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
-        case 128: return launch_d<LAYOUT, BITS, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
-        case 256: return launch_d<LAYOUT, BITS, 256, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 64: return launch_d<LAYOUT, BITS, 64, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 128: return launch_d<LAYOUT, BITS, 128, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
+        case 256: return launch_d<LAYOUT, BITS, 256, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
         default: break;
     }
     return hipErrorInvalidValue;
@@ -1818,9 +1795,37 @@ int pick_variant(int layout, int bits, int C, int B, int64_t keys, int D) {
 
 }  // namespace
 
+namespace {
+
+// The single-pass f16 form takes the automatic choice's family, with the
+// LDS-staged kernel where that choice is the register-resident one.
+int pick_f16_variant(int layout, int bits, int C, int B, int64_t keys, int D) {
+    const int v = pick_variant(layout, bits, C, B, keys, D);
+    return v == kMfmaReg ? kMfmaLds : v;
+}
+
+// The name of a kernel's single-pass f16 form (static strings).
+const char* with_f16_suffix(const char* base) {
+    if (!base) return nullptr;
+    static const char* const names[][2] = {
+        {"mfma32_unpacked_mt1", "mfma32_unpacked_mt1_f16"}, {"mfma32_unpacked_mt2", "mfma32_unpacked_mt2_f16"},
+        {"mfma32_unpacked_mt4", "mfma32_unpacked_mt4_f16"}, {"mfma32_packed2_mt1", "mfma32_packed2_mt1_f16"},
+        {"mfma32_packed2_mt2", "mfma32_packed2_mt2_f16"}, {"mfma32_packed2_mt4", "mfma32_packed2_mt4_f16"},
+        {"mfma32_packed3_mt1", "mfma32_packed3_mt1_f16"}, {"mfma32_packed3_mt2", "mfma32_packed3_mt2_f16"},
+        {"mfma32_packed3_mt4", "mfma32_packed3_mt4_f16"}, {"mfma16_unpacked", "mfma16_unpacked_f16"},
+        {"mfma16_packed2", "mfma16_packed2_f16"}, {"mfma16_packed3", "mfma16_packed3_f16"},
+        {"mfma32shared_unpacked", "mfma32shared_unpacked_f16"}, {"mfma32shared_packed2", "mfma32shared_packed2_f16"},
+        {"mfma32shared_packed3", "mfma32shared_packed3_f16"},
+    };
+    for (const auto& n : names)
+        if (__builtin_strcmp(n[0], base) == 0) return n[1];
+    return nullptr;
+}
+}  // namespace
+
 bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant) {
     (void)B;
-    if (variant == kMfmaAuto) return lds_supported(layout, bits, C, D);
+    if (variant == kMfmaAuto || variant == kMfmaF16) return lds_supported(layout, bits, C, D);
     if (variant == kMfmaLds) return lds_supported(layout, bits, C, D);
     if (variant == kMfmaReg) return reg_supported(layout, bits, C, D);
     if (variant == kMfmaSmall) return small_supported(layout, bits, C, D);
@@ -1830,6 +1835,9 @@ bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant
 
 const char* score_mfma_name(int layout, int bits, int C, int P, int B, int S, int D, int variant) {
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return nullptr;
+    if (variant == kMfmaF16)
+        return with_f16_suffix(score_mfma_name(layout, bits, C, P, B, S, D,
+                                               pick_f16_variant(layout, bits, C, B, (int64_t)P * S, D)));
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
     if (variant == kMfmaReg) return layout == 0 ? "mfma32reg_unpacked" : bits == 2 ? "mfma32reg_packed2" : "mfma32reg_packed3";
     if (variant == kMfmaSmall) return layout == 0 ? "mfma16_unpacked" : bits == 2 ? "mfma16_packed2" : "mfma16_packed3";
@@ -1845,6 +1853,22 @@ hipError_t launch_score_mfma(const float* A, const float* T, KeyStreams keys,
                              float* scores, int P, int B, int S, int D, int variant,
                              hipStream_t stream) {
     if (!score_mfma_supported(layout, bits, C, B, D, variant)) return hipErrorInvalidValue;
+    if (variant == kMfmaF16) {
+        const int v = pick_f16_variant(layout, bits, C, B, (int64_t)P * S, D);
+        if (v == kMfmaShared) {
+            if (layout == 0) return launch_shared_layout<0, 0, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+            if (bits == 2) return launch_shared_layout<1, 2, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+            return launch_shared_layout<1, 3, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        }
+        if (v == kMfmaSmall) {
+            if (layout == 0) return launch_small_layout<0, 0, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+            if (bits == 2) return launch_small_layout<1, 2, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+            return launch_small_layout<1, 3, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        }
+        if (layout == 0) return launch_layout<0, 0, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        if (bits == 2) return launch_layout<1, 2, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+        return launch_layout<1, 3, true, true>(A, T, keys, codebook, C, scores, P, B, S, D, stream);
+    }
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
     if (variant == kMfmaShared) {
         if (layout == 0) return launch_shared_layout<0, 0>(A, T, keys, codebook, C, scores, P, B, S, D, stream);

@@ -38,8 +38,10 @@ hipError_t launch_score_valu(const float* A, const float* T, KeyStreams keys,
 // Matrix-core kernels come in three variants: 32x32 tiles with the query-side
 // operands staged once per workgroup in LDS, 32x32 tiles with them held in each
 // wavefront's registers, and 16x16 tiles for a few queries per problem.
-// kMfmaAuto picks by shape.
-enum MfmaVariant { kMfmaAuto = 0, kMfmaLds = 1, kMfmaReg = 2, kMfmaSmall = 3, kMfmaShared = 4 };
+// kMfmaAuto picks by shape. kMfmaF16 is the single-pass f16 form of the
+// automatic choice (one f16 product per contraction; the register variant's
+// shapes take the LDS-staged kernel).
+enum MfmaVariant { kMfmaAuto = 0, kMfmaLds = 1, kMfmaReg = 2, kMfmaSmall = 3, kMfmaShared = 4, kMfmaF16 = 5 };
 
 // Returns false if the variant does not cover (layout, bits, C, B, D).
 bool score_mfma_supported(int layout, int bits, int C, int B, int D, int variant);

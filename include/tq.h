@@ -145,6 +145,17 @@ int tq_score(const float* A, const float* T, const tq_keys* keys,
                                     tile through LDS (the MFMA shapes above with
                                     D in {64, 128}); the automatic choice for
                                     B > 96 */
+#define TQ_KERNEL_MFMA_F16 7  /* NOT fp32-accurate: the single-pass f16 form of the
+                                 automatic matrix-core choice (the MFMA shapes
+                                 above; the LDS-staged kernel where the automatic
+                                 choice is the register one). A and the codebook
+                                 enter as one f16 product, T and the signs as one
+                                 (the 16x16 form also keeps the query's lo rows,
+                                 which share its instructions), after the same
+                                 power-of-two scaling. Its contract is max over
+                                 elements of |got - exact| / (1 + |exact|) <= 2e-2
+                                 instead of tq_score's 1e-4: a reported comparison
+                                 point, never chosen by TQ_KERNEL_AUTO. */
 
 /*
  * tq_score_with_kernel: tq_score with an explicit kernel family, so that every

@@ -98,7 +98,7 @@ void scoring() {
     // names are pure queries: any input, including the int32 extremes, gives a name or NULL
     const int ext[] = {INT_MIN, -1, 0, 1, 31, 32, 33, 65535, 65536, 262144, 262145, (1 << 24) - 1, 1 << 24, INT_MAX};
     const int kernels[] = {TQ_KERNEL_AUTO, TQ_KERNEL_VALU, TQ_KERNEL_MFMA, TQ_KERNEL_MFMA_LDS, TQ_KERNEL_MFMA_REG,
-                           TQ_KERNEL_MFMA16, TQ_KERNEL_MFMA_SHARED, 99};
+                           TQ_KERNEL_MFMA16, TQ_KERNEL_MFMA_SHARED, TQ_KERNEL_MFMA_F16, 99};
     for (int P : ext)
         for (int B : ext)
             for (int S : ext)

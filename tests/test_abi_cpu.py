@@ -72,6 +72,14 @@ def test_kernel_names_host_only():
     assert n("packed", 2, 4, 1, 32, 100, 48, "mfma") is None
     assert n("packed", 2, 8, 1, 32, 100, 128) is None      # C != 2^bits
     assert n("packed", 4, 16, 1, 32, 100, 128) is None     # 4-bit not supported
+    # the single-pass f16 form follows the automatic choice (register shapes take the LDS kernel)
+    assert n("unpacked", 0, 4, 1, 32, 32768, 128, "mfma_f16") == "mfma32_unpacked_mt1_f16"
+    assert n("packed", 2, 4, 1, 32, 131072, 128, "mfma_f16") == "mfma32_packed2_mt1_f16"
+    assert n("packed", 3, 8, 128, 4, 32768, 128, "mfma_f16") == "mfma16_packed3_f16"
+    assert n("packed", 3, 8, 1, 128, 262144, 128, "mfma_f16") == "mfma32shared_packed3_f16"
+    assert n("packed", 3, 8, 1, 64, 262144, 128, "mfma_f16") == "mfma32_packed3_mt2_f16"
+    assert n("unpacked", 0, 4, 1, 2, 256, 32, "mfma_f16") == "mfma32_unpacked_mt1_f16"
+    assert n("unpacked", 0, 16, 1, 32, 100, 128, "mfma_f16") is None      # C > 8
 
 
 def _keys(layout=0, bits=0, idx=16, sign=16, gamma=16):
@@ -90,7 +98,7 @@ def test_score_rejects_bad_arguments_before_launch():
     assert _score(_keys(layout=5)) == ARG
     assert _score(_keys(), S=-1) == ARG
     assert _score(_keys(), D=0) == ARG
-    assert _score(_keys(), kernel=7) == ARG
+    assert _score(_keys(), kernel=8) == ARG
     assert _score(_keys(), kernel=-1) == ARG
     assert _score(_keys(), S=1 << 24, kernel=2) == UNSUP
     assert _score(_keys(layout=1, bits=4), C=16) == UNSUP
