@@ -955,7 +955,12 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
         const float4 v = *reinterpret_cast<const float4*>(src + k);
         x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
     }
-    TileCodes<NI, NS> codes[3];               // code buffers of the tile loop
+    // Code buffers of the tile loop: a packed tile's codes are 3-5 registers a
+    // lane, so five buffers (four tiles in flight) fit the four wavefronts per
+    // SIMD the launch asks for (GQA: 104.0 -> 99.1 us against three); unpacked
+    // codes (17 registers) and the six-wavefront MSE form keep three.
+    constexpr int NBUF = (QJL && LAYOUT == 1) ? 5 : 3;
+    TileCodes<NI, NS> codes[NBUF];
     TileCodes<NI, NS>& cur = codes[0];
     asm volatile("" ::: "memory");
     load_quarter<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
@@ -1054,13 +1059,14 @@ __global__ __launch_bounds__(kThreads, MINW) void score_mfma16_kernel(
             store_score(out_r, off, (kx * c.gam) * ((acc[0] + acc[1]) + acc[2]));
     };
 
-    // three code buffers in turn: each tile's codes are requested two tiles ahead
+    // NBUF code buffers in turn: each tile's codes are requested NBUF - 1 tiles ahead
     auto load = [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
         load_quarter<LAYOUT, BITS, D, QJL>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys16 + kc, S - 1),
                                            gq);
     };
-    load(codes[1], tile + stride);
-    rotate_tiles<3>(codes, tile, stride, ntiles, load, tile_scores);
+#pragma unroll
+    for (int k = 1; k < NBUF - 1; ++k) load(codes[k], tile + k * stride);
+    rotate_tiles<NBUF>(codes, tile, stride, ntiles, load, tile_scores);
 }
 
 // ---------------------------------------------------------------------------
