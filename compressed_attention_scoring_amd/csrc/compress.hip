@@ -23,6 +23,12 @@
 //   5. p = S_mat r              (A = S_mat rows, B = r)
 //   6. sign = (p >= 0)          (a zero projection counts as +1)
 //   7. pack and store           (through LDS, one lane per 32 coordinates of a key)
+// Pi and S_mat of the workgroup's head are staged in LDS once (fp32, rows padded
+// by 16 bytes so that rows read at the same column by different lanes fall in
+// different banks: 132 KiB at D = 128), and the workgroup's wavefronts then walk
+// 16-key tiles, reading every A operand from LDS: read from L2 instead (the
+// former form), each wavefront fetched 192 KiB of matrix data per tile with 576
+// load instructions. Every operand address is one per-lane base plus a constant.
 // v_mfma_f64_16x16x4_f64 holds A[row][slot] in lane 16 slot + row, B[slot][col]
 // in lane 16 slot + col, and output register v of lane 16 q + col at row 4 v + q
 // (a layout checked on the device). So after a product, lane group q = lane / 16
@@ -62,7 +68,15 @@ template <int D>
 struct CompressLds {
     static constexpr int BYTES = kKeysPerWave * D;          // idx or sign bytes of 16 keys
     static constexpr int PER_WAVE = 2 * BYTES;
+    static constexpr int LD = D + 4;                         // staged row stride (floats)
+    static constexpr int MAT = D * LD;                       // floats of one staged matrix
 };
+
+// LDS position of element (row, c) of a staged D x D matrix.
+template <int D>
+__device__ __forceinline__ int staged(int row, int c) {
+    return row * CompressLds<D>::LD + c;
+}
 
 template <int D, int LAYOUT, int BITS, int NC>
 __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
@@ -72,22 +86,35 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     constexpr int RB = D / 16;                 // 16-row output blocks
     constexpr int KQ = D / 16;                 // 16-wide contraction chunks (4 MFMAs each)
     using L = CompressLds<D>;
+    __shared__ __attribute__((aligned(16))) float mats[2 * L::MAT];   // Pi_h, then S_mat_h (staged())
     __shared__ __attribute__((aligned(16))) uint8_t lds[kCompressWaves * L::PER_WAVE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int p = blockIdx.y;
     const int h = p % H;
-    const int s0 = (blockIdx.x * kCompressWaves + wave) * kKeysPerWave;
-    if (s0 >= S) return;                       // no barrier in this kernel
-    const int q = lane >> 4;                   // contraction slot / output row group
-    const int col = lane & 15;                 // key column
-    const int key = min(s0 + col, S - 1);      // clamped: keys past S are computed, not stored
-    const float* kp = keys + ((int64_t)p * S + key) * D;
-    const float* Pp = Pi + (int64_t)h * D * D;
-    const float* Sp = Smat + (int64_t)h * D * D;
+    const float* Pp = mats;
+    const float* Sp = mats + L::MAT;
+    {
+        const float4* gp = reinterpret_cast<const float4*>(Pi + (int64_t)h * D * D);
+        const float4* gs = reinterpret_cast<const float4*>(Smat + (int64_t)h * D * D);
+        for (int i = threadIdx.x; i < D * D / 4; i += kCompressWaves * 64) {
+            const int row = i / (D / 4), c = 4 * (i % (D / 4));
+            const float4 a = gp[i], b = gs[i];
+            *reinterpret_cast<float4*>(mats + staged<D>(row, c)) = a;
+            *reinterpret_cast<float4*>(mats + L::MAT + staged<D>(row, c)) = b;
+        }
+    }
+    __syncthreads();                           // the only barrier: the matrices are read-only below
     uint8_t* ibuf = lds + wave * L::PER_WAVE;                  // [16][D] indices
     uint8_t* sbuf = ibuf + L::BYTES;                            // [16][D] sign bits (0/1)
+    const int q = lane >> 4;                   // contraction slot / output row group
+    const int col = lane & 15;                 // key column
+
+    for (int s0 = (blockIdx.x * kCompressWaves + wave) * kKeysPerWave; s0 < S;
+         s0 += gridDim.x * kCompressWaves * kKeysPerWave) {
+    const int key = min(s0 + col, S - 1);      // clamped: keys past S are computed, not stored
+    const float* kp = keys + ((int64_t)p * S + key) * D;
 
     // ---- 0. the key's length: this lane holds coordinates j = 16 kq + 4 q + t
     //      (the order of the first product), the four lane groups the rest
@@ -117,7 +144,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
         const double u2 = (double)kv[kq].z / div, u3 = (double)kv[kq].w / div;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float4 av = *reinterpret_cast<const float4*>(Pp + (int64_t)(16 * rb + col) * D + 16 * kq + 4 * q);
+            const float4 av = *reinterpret_cast<const float4*>(Pp + staged<D>(16 * rb + col, 16 * kq + 4 * q));
             acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.x, u0, acc[rb], 0, 0, 0);
             acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.y, u1, acc[rb], 0, 0, 0);
             acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av.z, u2, acc[rb], 0, 0, 0);
@@ -158,10 +185,10 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     for (int kq = 0; kq < KQ; ++kq) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float* prow = Pp + (int64_t)(16 * kq + 4 * t + q) * D + col;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)prow[16 * rb], cr[kq][t], acc[rb], 0, 0, 0);
+                acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)Pp[staged<D>(16 * kq + 4 * t + q, 16 * rb + col)],
+                                                             cr[kq][t], acc[rb], 0, 0, 0);
         }
     }
     // ---- 4. r = u - x (acc[rb][v] = x[j = 16 rb + 4 v + q] of key col), gamma;
@@ -187,10 +214,10 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
     for (int kq = 0; kq < KQ; ++kq) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float* srow = Sp + (int64_t)(16 * rb + col) * D + 16 * kq + q;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)srow[4 * t], cr[kq][t], acc[rb], 0, 0, 0);
+                acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)Sp[staged<D>(16 * rb + col, 16 * kq + q + 4 * t)],
+                                                             cr[kq][t], acc[rb], 0, 0, 0);
         }
     }
     // ---- 6. sign bits (1 = +1, also for an exactly zero projection) of
@@ -266,13 +293,24 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(
             }
         }
     }
+    // the next tile's index and sign bytes go to the same LDS rows: every lane's
+    // packing reads above come first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 }
 
 template <int D, int LAYOUT, int BITS>
 hipError_t launch_compress_d(const float* keys, const float* Pi, const float* S_mat, const float* codebook,
                              int C, KeyOut out, int P, int H, int S, hipStream_t stream) {
+    // about one workgroup per compute unit (each stages its head's two matrices,
+    // 128 KiB at D = 128, once), its wavefronts walking 16-key tiles
     const int per_block = kCompressWaves * kKeysPerWave;
-    const dim3 grid((unsigned)((S + per_block - 1) / per_block), (unsigned)P);
+    int64_t gx = (S + per_block - 1) / per_block;
+    const int64_t cap = 256 / P > 0 ? 256 / P : 1;
+    if (gx > cap) gx = cap;
+    const dim3 grid((unsigned)gx, (unsigned)P);
     // codebook registers sized to the codebook: 8 entries cover every packed format
     if (C <= 8)
         hipLaunchKernelGGL((compress_kernel<D, LAYOUT, BITS, 8>), grid, dim3(kCompressWaves * 64), 0, stream,
