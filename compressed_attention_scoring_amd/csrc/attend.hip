@@ -61,7 +61,7 @@ constexpr float kTau = 5.5f;       // rescale when a step max passes the referen
 constexpr int kNormBits = 4;       // scaled norms stay below 2^(kNormBits + 2) until the next rescale
 constexpr int kTargetBlocks = 512; // workgroups one call aims for (two per compute unit)
 constexpr int kComputeUnits = 256; // MI355X
-constexpr int kPartialShare = 4;   // partial results at most 1/4 of the bytes a chunk reads
+constexpr int kPartialShare = 8;   // partial results at most 1/8 of the bytes a chunk reads
 
 union H8 {
     f16x8 h;
@@ -555,6 +555,13 @@ Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
     const int ntfull = D / rows;
     pl.dblk = 1;
     while (pl.dblk < 4 && ntfull / (2 * pl.dblk) >= 1 && blocks * n * pl.dblk < kComputeUnits) pl.dblk *= 2;
+    // and past one round, whole rounds again (fewer, longer chunks rather than a
+    // partial round: packed workload 320 -> 256 workgroups)
+    const int64_t wgs = blocks * n * pl.dblk;
+    if (wgs > kComputeUnits && wgs % kComputeUnits != 0) {
+        const int64_t n2 = wgs / kComputeUnits * kComputeUnits / (blocks * pl.dblk);
+        if (n2 >= 1) n = n2;
+    }
     pl.nt = ntfull / pl.dblk;
     const int64_t per = (S + n - 1) / n;
     pl.chunk = (int)((per + unit - 1) / unit * unit);
