@@ -61,7 +61,10 @@ constexpr float kTau = 5.5f;       // rescale when a step max passes the referen
 constexpr int kNormBits = 4;       // scaled norms stay below 2^(kNormBits + 2) until the next rescale
 constexpr int kTargetBlocks = 512; // workgroups one call aims for (two per compute unit)
 constexpr int kComputeUnits = 256; // MI355X
-constexpr int kPartialShare = 8;   // partial results at most 1/8 of the bytes a chunk reads
+// Partial results at most 1/kPartialShare of the bytes a chunk reads, or
+// 1/kPartialShareWide where the smaller share would leave fewer workgroups.
+constexpr int kPartialShare = 8;
+constexpr int kPartialShareWide = 4;
 
 union H8 {
     f16x8 h;
@@ -525,7 +528,7 @@ struct Plan {
     int nmax;    // chunk count before rounding (an upper bound on nch)
 };
 
-Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
+Plan make_plan_share(int P, int B, int S, int D, int layout, int bits, int share) {
     Plan pl;
     pl.mode = B <= 8 ? kNarrow : kWide;
     const int Q = pl.mode == kWide ? Geo<kWide>::Q : Geo<kNarrow>::Q;
@@ -535,11 +538,11 @@ Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
     pl.qtw = ntiles >= 4 ? 4 : ntiles >= 2 ? 2 : 1;
     pl.gy = (ntiles + pl.qtw - 1) / pl.qtw;
     const int unit = kstep * (kWaves / pl.qtw);      // keys of one step of every wavefront sharing a tile
-    // keys per chunk at least: the partial results stay under 1/kPartialShare of
+    // keys per chunk at least: the partial results stay under 1/share of
     // the bytes the chunk reads (its scores and values)
     const int64_t bq = std::min<int64_t>(B, (int64_t)Q * pl.qtw);
     const int64_t vbytes = (layout == 0 ? D + 4 : (int64_t)D * bits / 8 + 2);
-    int64_t cmin = (kPartialShare * bq * (D + 2) * 4 + bq * 4 + vbytes - 1) / (bq * 4 + vbytes);
+    int64_t cmin = (share * bq * (D + 2) * 4 + bq * 4 + vbytes - 1) / (bq * 4 + vbytes);
     cmin = (cmin + unit - 1) / unit * unit;
     const int64_t blocks = (int64_t)P * pl.gy;
     int64_t n = (kTargetBlocks + blocks - 1) / blocks;
@@ -567,6 +570,20 @@ Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
     pl.chunk = (int)((per + unit - 1) / unit * unit);
     pl.nch = (int)(((int64_t)S + pl.chunk - 1) / pl.chunk);
     pl.nmax = (int)n;
+    return pl;
+}
+
+// The smaller record share where it keeps the workgroup count (decode: 64
+// chunks x 4 coordinate blocks instead of 128 x 2), the larger one where it
+// would halve it (long: 256 workgroups instead of 512 ran no faster and fetched
+// 229 MB instead of 165 MB of scores and values).
+Plan make_plan(int P, int B, int S, int D, int layout, int bits) {
+    const Plan narrow = make_plan_share(P, B, S, D, layout, bits, kPartialShare);
+    const Plan wide = make_plan_share(P, B, S, D, layout, bits, kPartialShareWide);
+    const int64_t wg_narrow = (int64_t)narrow.nch * narrow.gy * narrow.dblk;
+    const int64_t wg_wide = (int64_t)wide.nch * wide.gy * wide.dblk;
+    Plan pl = wg_narrow >= wg_wide ? narrow : wide;
+    pl.nmax = narrow.nmax > wide.nmax ? narrow.nmax : wide.nmax;   // an upper bound on either's chunks
     return pl;
 }
 
