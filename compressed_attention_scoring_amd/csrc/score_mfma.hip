@@ -671,6 +671,75 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
 // workgroup barrier per tile. This removes the fourfold key decoding of the
 // register variant, whose main loop was bound by vector-ALU issue.
 // ---------------------------------------------------------------------------
+// Coalesced loading of one wavefront's 32 query rows into the register layout
+// in which lane (col, g) holds row col's coordinates [g D/2, (g+1) D/2). Loading
+// that half row directly makes each load instruction touch 64 different
+// 128-byte lines, one per lane; with every workgroup re-reading all of A and T
+// that prologue took about a fifth of the long launch (timeline stamps: operands
+// ready ~8 us after the first wave starts). Here each instruction reads whole
+// lines of consecutive rows, and a transpose through the wavefront's own LDS
+// region hands every lane its half row. Chunk c holds the CW/2 columns from
+// c CW/2 on of both halves of all 32 rows; 16-byte slots are XOR-swizzled by row
+// so that neither the writes nor the reads conflict on banks.
+template <int D, int CW>
+struct RowStage {
+    static constexpr int HALF = D / 2;
+    static constexpr int NSL = CW / 4;            // 16-byte slots per staged row
+    static constexpr int NCH = HALF / (CW / 2);   // chunks per matrix
+    static constexpr int PER = CW / 8;            // 16-byte loads per lane per chunk
+    static constexpr int BYTES = 32 * CW * 4;     // LDS region per wavefront
+    static_assert(CW == 32 || CW == 64, "16 or 8 slots per staged row");
+    static_assert(HALF % (CW / 2) == 0, "chunks tile each half row");
+
+    // slot of (row r, slot q): rows that one 16-lane LDS pass touches land on
+    // distinct 4-bank groups (two rows share the 64 banks when CW = 32)
+    __device__ static __forceinline__ int swz(int r, int q) { return q ^ ((r / (16 / NSL)) % NSL); }
+
+    // Requests this lane's part of chunk c of the matrix whose wavefront rows
+    // start at `rows`; row r reads row min(r, last) (rows past the end re-read
+    // a valid one and are never stored).
+    __device__ static __forceinline__ void load(const float* rows, int last, int lane, int c, float (&v)[4 * PER]) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int f = i * 64 + lane;
+            const int r = f / NSL, q = f % NSL;
+            const int h = q / (NSL / 2), w = q % (NSL / 2);
+            const float4 x = *reinterpret_cast<const float4*>(rows + (int64_t)min(r, last) * D + h * HALF + c * (CW / 2) + w * 4);
+            v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+        }
+    }
+
+    // Writes chunk c to the wavefront's region and reads back this lane's
+    // columns of it into dst[c CW/2 ...]. The region is private to the
+    // wavefront, so wavefront-scope ordering suffices; the second fence keeps
+    // the next chunk's writes behind this chunk's reads.
+    __device__ static __forceinline__ void transpose(uint8_t* region, int lane, int c, const float (&v)[4 * PER],
+                                                     float (&dst)[HALF]) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int f = i * 64 + lane;
+            const int r = f / NSL, q = f % NSL;
+            *reinterpret_cast<float4*>(region + r * CW * 4 + swz(r, q) * 16) =
+                make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int col = lane & 31, g = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const float4 x = *reinterpret_cast<const float4*>(region + col * CW * 4 + swz(col, g * (NSL / 2) + i) * 16);
+            dst[c * (CW / 2) + 4 * i] = x.x;
+            dst[c * (CW / 2) + 4 * i + 1] = x.y;
+            dst[c * (CW / 2) + 4 * i + 2] = x.z;
+            dst[c * (CW / 2) + 4 * i + 3] = x.w;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+};
+
 // Per k-step LDS blocks: the codebook's hi part, its lo part unless F16, and
 // the signs with QJL.
 template <int LAYOUT, int BITS, int D, bool QJL = true, bool F16 = false>
@@ -740,19 +809,38 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     const int stride = gridDim.x;
     if (tile >= ntiles) return;
 
-    // query half rows (clamped to a valid row; wavefronts past B never store)
-    const int64_t roff = ((int64_t)p * B + min(b0 + col, B - 1)) * D + g * HALF;
+    // Query half rows (rows past B re-read row B - 1; wavefronts past B never
+    // store). Both LDS buffers serve as the staging area of the coalesced load
+    // when they hold a 4 KiB region per wavefront; one barrier then frees them
+    // for the first tile.
+    constexpr bool STAGED = 2 * L::BUF / kWaves >= RowStage<D, 32>::BYTES;
+    using RS = RowStage<D, (2 * L::BUF / kWaves >= RowStage<D, 64>::BYTES) ? 64 : 32>;
+    static_assert(!STAGED || kWaves * RS::BYTES <= 2 * L::BUF, "staging regions fit the LDS buffers");
     float a[HALF], t[HALF];
+    float va[RS::NCH][4 * RS::PER], vt[RS::NCH][4 * RS::PER];
+    const int last = B - 1 - b0;
+    if constexpr (STAGED) {
 #pragma unroll
-    for (int k = 0; k < HALF; k += 4) {
-        const float4 va = *reinterpret_cast<const float4*>(A + roff + k);
-        a[k] = va.x; a[k + 1] = va.y; a[k + 2] = va.z; a[k + 3] = va.w;
+        for (int c = 0; c < RS::NCH; ++c) RS::load(A + ((int64_t)p * B + b0) * D, last, lane, c, va[c]);
         if constexpr (QJL) {
-            const float4 vt = *reinterpret_cast<const float4*>(T + roff + k);
-            t[k] = vt.x; t[k + 1] = vt.y; t[k + 2] = vt.z; t[k + 3] = vt.w;
-        } else {
-            t[k] = t[k + 1] = t[k + 2] = t[k + 3] = 0.f;
+#pragma unroll
+            for (int c = 0; c < RS::NCH; ++c) RS::load(T + ((int64_t)p * B + b0) * D, last, lane, c, vt[c]);
         }
+    } else {
+        const int64_t roff = ((int64_t)p * B + min(b0 + col, B - 1)) * D + g * HALF;
+#pragma unroll
+        for (int k = 0; k < HALF; k += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(A + roff + k);
+            a[k] = x.x; a[k + 1] = x.y; a[k + 2] = x.z; a[k + 3] = x.w;
+            if constexpr (QJL) {
+                const float4 y = *reinterpret_cast<const float4*>(T + roff + k);
+                t[k] = y.x; t[k + 1] = y.y; t[k + 2] = y.z; t[k + 3] = y.w;
+            }
+        }
+    }
+    if constexpr (!QJL) {
+#pragma unroll
+        for (int k = 0; k < HALF; ++k) t[k] = 0.f;
     }
     TileCodes<NI, NS> c0, c1;
     asm volatile("" ::: "memory");
@@ -763,6 +851,16 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     float sc;
     uint32_t tab_hi[4], tab_lo[4];
     codebook_tables(codebook, C, sc, tab_hi, tab_lo);
+    if constexpr (STAGED) {
+        uint8_t* region = kops + wave * RS::BYTES;
+#pragma unroll
+        for (int c = 0; c < RS::NCH; ++c) RS::transpose(region, lane, c, va[c], a);
+        if constexpr (QJL) {
+#pragma unroll
+            for (int c = 0; c < RS::NCH; ++c) RS::transpose(region, lane, c, vt[c], t);
+        }
+        __syncthreads();
+    }
 
     float ma = 0.f, mt = 0.f;
 #pragma unroll
