@@ -385,6 +385,35 @@ struct TileCodes {
     float gam;
 };
 
+// Four-query kernels (16 x 16 MFMA tiles, 16 keys per tile): lane group
+// gq = lane / 16 owns coordinates [gq D/4, (gq + 1) D/4) of each key and reads
+// its quarter of the key's index and sign rows.
+constexpr int kTileKeys16 = 16;
+
+template <int LAYOUT, int BITS, int D>
+struct SmallFmt {
+    using F = Fmt<LAYOUT, BITS>;
+    static constexpr int Q = D / 4;                            // coordinates per lane
+    static constexpr int NI = F::template idx_dw<D / 2>();     // code dwords per lane
+    static constexpr int NS = F::template sign_dw<D / 2>();
+    static constexpr int IDX_ROW = F::template idx_row<D>();
+    static constexpr int SIGN_ROW = F::template sign_row<D>();
+    static constexpr int NJ = Q / 8;                           // k-steps of 8 coordinates per lane
+};
+
+template <int LAYOUT, int BITS, int D, bool QJL = true>
+__device__ __forceinline__ void load_quarter(TileCodes<SmallFmt<LAYOUT, BITS, D>::NI, SmallFmt<LAYOUT, BITS, D>::NS>& c,
+                                             const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+                                             const void* __restrict__ gamma, int64_t key, int gq) {
+    using SF = SmallFmt<LAYOUT, BITS, D>;
+    constexpr int IQ = SF::IDX_ROW / 4, SQ = SF::SIGN_ROW / 4;
+    load_dwords<SF::NI, align_of_seg(SF::IDX_ROW, IQ)>(idx + key * SF::IDX_ROW + gq * IQ, c.iw);
+    if constexpr (QJL) load_dwords<SF::NS, align_of_seg(SF::SIGN_ROW, SQ)>(sign + key * SF::SIGN_ROW + gq * SQ, c.sw);
+    if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
+    else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
+}
+
+
 // Key-side operands of k-step j: codebook hi and lo parts looked up by index,
 // and signs as f16 +-1. LO = false (the single-pass f16 kernels) skips the lo
 // part and leaves `clo` untouched.

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "mfma_layout.hpp"
+#include "score_i8.hpp"
 #include "value_sel.hpp"
 
 namespace tq {
@@ -993,32 +994,6 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
 // qjl_dim over a D/2-coordinate half, here used on a D/4 quarter).
 // Query groups of four beyond the first (B = 5..8) are further workgroup rows.
 // ---------------------------------------------------------------------------
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kTileKeys16 = 16;
-
-template <int LAYOUT, int BITS, int D>
-struct SmallFmt {
-    using F = Fmt<LAYOUT, BITS>;
-    static constexpr int Q = D / 4;                            // coordinates per lane
-    static constexpr int NI = F::template idx_dw<D / 2>();     // code dwords per lane
-    static constexpr int NS = F::template sign_dw<D / 2>();
-    static constexpr int IDX_ROW = F::template idx_row<D>();
-    static constexpr int SIGN_ROW = F::template sign_row<D>();
-    static constexpr int NJ = Q / 8;                           // k-steps of 8 coordinates per lane
-};
-
-template <int LAYOUT, int BITS, int D, bool QJL = true>
-__device__ __forceinline__ void load_quarter(TileCodes<SmallFmt<LAYOUT, BITS, D>::NI, SmallFmt<LAYOUT, BITS, D>::NS>& c,
-                                             const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
-                                             const void* __restrict__ gamma, int64_t key, int gq) {
-    using SF = SmallFmt<LAYOUT, BITS, D>;
-    constexpr int IQ = SF::IDX_ROW / 4, SQ = SF::SIGN_ROW / 4;
-    load_dwords<SF::NI, align_of_seg(SF::IDX_ROW, IQ)>(idx + key * SF::IDX_ROW + gq * IQ, c.iw);
-    if constexpr (QJL) load_dwords<SF::NS, align_of_seg(SF::SIGN_ROW, SQ)>(sign + key * SF::SIGN_ROW + gq * SQ, c.sw);
-    if constexpr (LAYOUT == 0) c.gam = reinterpret_cast<const float*>(gamma)[key];
-    else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
-}
-
 // QJL = false (MSE-only keys, gamma = the key's norm, no sign stream): row
 // types 0 and 1 stay A_hi and A_lo against the codebook's hi part in elements
 // 0-3, type 2 is A_hi against its lo part in elements 4-7, type 3 is zero, so
@@ -1785,6 +1760,9 @@ hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const fl
 template <int LAYOUT, int BITS, bool QJL = true, bool F16 = false>
 hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                                int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
+    // packed keys with signs: the integer form (three int8 limbs per operand)
+    if constexpr (LAYOUT == 1 && QJL && !F16)
+        return launch_score_i8(A, T, k, codebook, C, scores, P, B, S, D, BITS, stream);
     if (D == 128) return launch_small_d<LAYOUT, BITS, 128, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     if (D == 256) return launch_small_d<LAYOUT, BITS, 256, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     return hipErrorInvalidValue;
@@ -1924,7 +1902,7 @@ const char* with_f16_suffix(const char* base) {
         {"mfma32_packed2_mt2", "mfma32_packed2_mt2_f16"}, {"mfma32_packed2_mt4", "mfma32_packed2_mt4_f16"},
         {"mfma32_packed3_mt1", "mfma32_packed3_mt1_f16"}, {"mfma32_packed3_mt2", "mfma32_packed3_mt2_f16"},
         {"mfma32_packed3_mt4", "mfma32_packed3_mt4_f16"}, {"mfma16_unpacked", "mfma16_unpacked_f16"},
-        {"mfma16_packed2", "mfma16_packed2_f16"}, {"mfma16_packed3", "mfma16_packed3_f16"},
+        {"mfma16i8_packed2", "mfma16_packed2_f16"}, {"mfma16i8_packed3", "mfma16_packed3_f16"},
         {"mfma32shared_unpacked", "mfma32shared_unpacked_f16"}, {"mfma32shared_packed2", "mfma32shared_packed2_f16"},
         {"mfma32shared_packed3", "mfma32shared_packed3_f16"},
     };
@@ -1951,7 +1929,7 @@ const char* score_mfma_name(int layout, int bits, int C, int P, int B, int S, in
                                                pick_f16_variant(layout, bits, C, B, (int64_t)P * S, D)));
     if (variant == kMfmaAuto) variant = pick_variant(layout, bits, C, B, (int64_t)P * S, D);
     if (variant == kMfmaReg) return layout == 0 ? "mfma32reg_unpacked" : bits == 2 ? "mfma32reg_packed2" : "mfma32reg_packed3";
-    if (variant == kMfmaSmall) return layout == 0 ? "mfma16_unpacked" : bits == 2 ? "mfma16_packed2" : "mfma16_packed3";
+    if (variant == kMfmaSmall) return layout == 0 ? "mfma16_unpacked" : bits == 2 ? "mfma16i8_packed2" : "mfma16i8_packed3";
     if (variant == kMfmaShared) return layout == 0 ? "mfma32shared_unpacked" : bits == 2 ? "mfma32shared_packed2" : "mfma32shared_packed3";
     const int mt = mt_for(B, D);
     if (layout == 0) return mt == 4 ? "mfma32_unpacked_mt4" : mt == 2 ? "mfma32_unpacked_mt2" : "mfma32_unpacked_mt1";

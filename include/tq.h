@@ -139,7 +139,10 @@ int tq_score(const float* A, const float* T, const tq_keys* keys,
 #define TQ_KERNEL_MFMA16   5  /* matrix cores, 16x16 tiles of four queries times
                                  their four operand rows (the MFMA shapes above
                                  with D in {128, 256}); the automatic choice for
-                                 B <= 4 with P * S >= 2^20 keys */
+                                 B <= 4 with P * S >= 2^20 keys. Packed keys run
+                                 on the int8 matrix cores, A, T and the codebook
+                                 split into three int8 limbs each (exact integer
+                                 products, the same 1e-4 contract) */
 #define TQ_KERNEL_MFMA_SHARED 6  /* matrix cores, four query tiles per workgroup in
                                     registers sharing one unpacking of each key
                                     tile through LDS (the MFMA shapes above with

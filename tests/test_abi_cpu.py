@@ -44,7 +44,7 @@ def test_kernel_names_host_only():
     n = tq.tq_score_kernel_name
     assert n("unpacked", 0, 4, 1, 32, 32768, 128) == "mfma32_unpacked_mt1"
     assert n("packed", 2, 4, 1, 32, 131072, 128) == "mfma32_packed2_mt1"
-    assert n("packed", 3, 8, 128, 4, 32768, 128) == "mfma16_packed3"
+    assert n("packed", 3, 8, 128, 4, 32768, 128) == "mfma16i8_packed3"
     assert n("packed", 3, 8, 128, 4, 32768, 128, "mfma_lds") == "mfma32_packed3_mt1"
     assert n("unpacked", 0, 4, 1, 4, 1 << 20, 128) == "mfma16_unpacked"
     assert n("unpacked", 0, 4, 1, 4, 32768, 128) == "mfma32_unpacked_mt1"     # few keys: LDS staging

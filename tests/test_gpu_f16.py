@@ -68,7 +68,8 @@ def test_f16_forms_follow_the_automatic_choice():
     for w in (synth.workload(x) for x in ("tiny", "decode", "packed", "gqa", "long")):
         auto = n(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D)
         f16 = n(w.layout, w.bits, w.C, w.P, w.B, w.S, w.D, "mfma_f16")
-        assert f16 == auto + "_f16", (w.name, auto, f16)
+        # the integer four-query kernel (packed keys) has its f16 form in the f16 four-query kernel
+        assert f16 == auto.replace("mfma16i8_", "mfma16_") + "_f16", (w.name, auto, f16)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "packed", "gqa", "long"])
