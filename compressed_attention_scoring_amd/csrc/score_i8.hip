@@ -81,7 +81,9 @@ __device__ __forceinline__ uint32_t put_byte(uint32_t w, int k, int v) {
     return w | (((uint32_t)v & 0xffu) << (8 * k));
 }
 
-template <int BITS, int D, int MINW>
+// QJL = false scores MSE-only keys (no sign stream, no T, gamma = the key's
+// norm): scores = norm M.
+template <int BITS, int D, int MINW, bool QJL>
 __global__ __launch_bounds__(kThreads, MINW) void score_i8_kernel(
     const float* __restrict__ A, const float* __restrict__ T,
     const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
@@ -115,16 +117,20 @@ __global__ __launch_bounds__(kThreads, MINW) void score_i8_kernel(
 #pragma unroll
     for (int k = 0; k < Q; k += 4) {
         const float4 va = *reinterpret_cast<const float4*>(A + qoff + k);
-        const float4 vt = *reinterpret_cast<const float4*>(T + qoff + k);
         xa[k] = va.x; xa[k + 1] = va.y; xa[k + 2] = va.z; xa[k + 3] = va.w;
-        xt[k] = vt.x; xt[k + 1] = vt.y; xt[k + 2] = vt.z; xt[k + 3] = vt.w;
+        if constexpr (QJL) {
+            const float4 vt = *reinterpret_cast<const float4*>(T + qoff + k);
+            xt[k] = vt.x; xt[k + 1] = vt.y; xt[k + 2] = vt.z; xt[k + 3] = vt.w;
+        } else {
+            xt[k] = xt[k + 1] = xt[k + 2] = xt[k + 3] = 0.f;
+        }
     }
     // Code buffers: each tile's codes are requested four tiles ahead (a packed
     // tile's codes are 3-5 registers a lane).
     constexpr int NBUF = 5;
     TileCodes<NI, NS> codes[NBUF];
     asm volatile("" ::: "memory");
-    load_quarter<1, BITS, D, true>(codes[0], idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
+    load_quarter<1, BITS, D, QJL>(codes[0], idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
     asm volatile("" ::: "memory");
 
     // codebook limb tables: tab[m] = limb m of entries 0-3 (dword 0) and 4-7
@@ -222,36 +228,43 @@ __global__ __launch_bounds__(kThreads, MINW) void score_i8_kernel(
                 }
                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(q, key, acc, 0, 0, 0);
             }
-            const uint32_t sw = c.sw[v / 2] >> (4 * (v % 2));
-            i32x4 bits, q;
+            if constexpr (QJL) {
+                const uint32_t sw = c.sw[v / 2] >> (4 * (v % 2));
+                i32x4 bits, q;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                bits[d] = (int)((sw >> d) & 0x01010101u);
-                q[d] = (int)ts[v][d];
+                for (int d = 0; d < 4; ++d) {
+                    bits[d] = (int)((sw >> d) & 0x01010101u);
+                    q[d] = (int)ts[v][d];
+                }
+                accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(q, bits, accs, 0, 0, 0);
             }
-            accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(q, bits, accs, 0, 0, 0);
         }
         // lane 16 q + key holds rows 4 q .. 4 q + 3 of column key: the weights 2^-7t
         const float M = weighted(acc[0], acc[1], acc[2], acc[3]);
-        const float Rb = weighted(accs[0], accs[1], accs[2], accs[3]);
         const int s = t * kTileKeys16 + kc;
         const uint32_t off = s < S ? ((uint32_t)gq * (uint32_t)S + (uint32_t)s) * 4u : kDropKey;
-        store_score(out_r, off, fmaf(ky * c.gam, fmaf(2.f, Rb, -tsum_out), kx * M));
+        if constexpr (QJL) {
+            const float Rb = weighted(accs[0], accs[1], accs[2], accs[3]);
+            store_score(out_r, off, fmaf(ky * c.gam, fmaf(2.f, Rb, -tsum_out), kx * M));
+        } else {
+            store_score(out_r, off, (kx * c.gam) * M);
+        }
     };
 
     auto load = [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
-        load_quarter<1, BITS, D, true>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys16 + kc, S - 1),
-                                       gq);
+        load_quarter<1, BITS, D, QJL>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys16 + kc, S - 1),
+                                      gq);
     };
 #pragma unroll
     for (int k = 1; k < NBUF - 1; ++k) load(codes[k], tile + k * stride);
     rotate_tiles<NBUF>(codes, tile, stride, ntiles, load, tile_scores);
 }
 
-template <int BITS, int D>
+template <int BITS, int D, bool QJL>
 hipError_t launch_bits_d(const float* A, const float* T, KeyStreams k, const float* codebook, int C, float* scores,
                          int P, int B, int S, hipStream_t stream) {
-    constexpr int MINW = D <= 128 ? 4 : 2;
+    // without signs about 77 registers at D = 128: six wavefronts per SIMD
+    constexpr int MINW = D <= 128 ? (QJL ? 4 : 6) : 2;
     const int groups_y = (B + 3) / 4;
     const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
     int64_t gx = (ntiles + kWaves - 1) / kWaves;
@@ -259,9 +272,20 @@ hipError_t launch_bits_d(const float* A, const float* T, KeyStreams k, const flo
     if (cap < 1) cap = 1;
     if (gx > cap) gx = cap;
     const float coef = (float)(kSqrtHalfPi / (double)D);
-    hipLaunchKernelGGL((score_i8_kernel<BITS, D, MINW>), dim3((unsigned)gx, groups_y, P), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((score_i8_kernel<BITS, D, MINW, QJL>), dim3((unsigned)gx, groups_y, P), dim3(kThreads), 0, stream,
                        A, T, k.idx, k.sign, k.gamma, codebook, C, scores, B, S, coef);
     return hipGetLastError();
+}
+
+
+template <bool QJL>
+hipError_t launch_qjl(const float* A, const float* T, KeyStreams k, const float* codebook, int C, float* scores,
+                      int P, int B, int S, int D, int bits, hipStream_t stream) {
+    if (bits == 2 && D == 128) return launch_bits_d<2, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (bits == 2 && D == 256) return launch_bits_d<2, 256, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (bits == 3 && D == 128) return launch_bits_d<3, 128, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    if (bits == 3 && D == 256) return launch_bits_d<3, 256, QJL>(A, T, k, codebook, C, scores, P, B, S, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -271,12 +295,9 @@ bool score_i8_supported(int layout, int bits, int C, int D) {
 }
 
 hipError_t launch_score_i8(const float* A, const float* T, KeyStreams k, const float* codebook, int C,
-                           float* scores, int P, int B, int S, int D, int bits, hipStream_t stream) {
-    if (bits == 2 && D == 128) return launch_bits_d<2, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (bits == 2 && D == 256) return launch_bits_d<2, 256>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (bits == 3 && D == 128) return launch_bits_d<3, 128>(A, T, k, codebook, C, scores, P, B, S, stream);
-    if (bits == 3 && D == 256) return launch_bits_d<3, 256>(A, T, k, codebook, C, scores, P, B, S, stream);
-    return hipErrorInvalidValue;
+                           float* scores, int P, int B, int S, int D, int bits, bool qjl, hipStream_t stream) {
+    return qjl ? launch_qjl<true>(A, T, k, codebook, C, scores, P, B, S, D, bits, stream)
+               : launch_qjl<false>(A, T, k, codebook, C, scores, P, B, S, D, bits, stream);
 }
 
 }  // namespace tq

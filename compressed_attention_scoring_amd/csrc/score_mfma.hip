@@ -1760,9 +1760,9 @@ hipError_t launch_small_d(const float* A, const float* T, KeyStreams k, const fl
 template <int LAYOUT, int BITS, bool QJL = true, bool F16 = false>
 hipError_t launch_small_layout(const float* A, const float* T, KeyStreams k, const float* codebook,
                                int C, float* scores, int P, int B, int S, int D, hipStream_t stream) {
-    // packed keys with signs: the integer form (three int8 limbs per operand)
-    if constexpr (LAYOUT == 1 && QJL && !F16)
-        return launch_score_i8(A, T, k, codebook, C, scores, P, B, S, D, BITS, stream);
+    // packed keys: the integer form (int8 limbs of every operand)
+    if constexpr (LAYOUT == 1 && !F16)
+        return launch_score_i8(A, T, k, codebook, C, scores, P, B, S, D, BITS, QJL, stream);
     if (D == 128) return launch_small_d<LAYOUT, BITS, 128, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     if (D == 256) return launch_small_d<LAYOUT, BITS, 256, QJL, F16>(A, T, k, codebook, C, scores, P, B, S, stream);
     return hipErrorInvalidValue;

@@ -110,3 +110,27 @@ def test_i8_limb_rounding_ties():
     err = run_case(3, C, D, P, B, S, rng, A, T, cb)
     say(f"i8 ties: max rel err {err:.2e}")
     assert err <= I8_TOL
+
+
+@pytest.mark.parametrize("bits,C,D", [(2, 4, 128), (3, 8, 128), (2, 4, 256), (3, 8, 256)])
+def test_i8_mse_only(bits, C, D):
+    """MSE-only keys (tq_score_mse: no signs, the stored norm scales M) on the
+    four-query shape, which takes the integer form for packed keys: every score
+    of a million-key launch within 1e-5 * (1 + |exact|)."""
+    from oracle import mse as om
+    from oracle import pack as opk
+    from oracle.codebook import codebook_fp32
+
+    say(f"i8 score_mse bits={bits} C={C} D={D}")
+    P, B, S = 8, 3, 131075
+    rng = np.random.default_rng([D, bits, 21])
+    idx = rng.integers(0, C, size=(P, S, D), dtype=np.uint8)
+    r = opk.gamma_to_half(rng.uniform(0.5, 2.0, size=(P, S)))
+    cb = codebook_fp32(D, C)
+    keys = tq.Values("packed", t(opk.pack_indices(idx, bits)), t(r), bits)
+    A = (rng.standard_normal((P, B, D)) * 3.0).astype(np.float32)
+    got = tq.tq_score_mse(t(A), keys, t(cb)).cpu().numpy()
+    err = max(rel_err(got[p], om.scores_mse_from_transformed(A[p].astype(np.float64), idx[p],
+                                                               r[p].astype(np.float64), cb)) for p in range(P))
+    say(f"i8 score_mse: max rel err {err:.2e}")
+    assert err <= I8_TOL
