@@ -656,6 +656,15 @@ def mse_bytes(w) -> int:
     return w.P * w.S * per_key + w.P * w.B * w.D * 4 + w.C * 4 + w.P * w.B * w.S * 4
 
 
+def score_dtype(kname) -> str:
+    """The arithmetic of a score kernel, from its name: the four-query kernel for
+    packed keys multiplies int8 limbs on the integer matrix cores, the others
+    f16 hi/lo parts on the f16 ones."""
+    if kname and "i8" in kname:
+        return "i8 MFMA on int8-limb-split fp32 operands (4 query limbs, 3 codebook limbs), i32 accumulate"
+    return "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate"
+
+
 def bench_mse(args, w, device) -> dict:
     """One step = tq_query_transform_hadamard + tq_score_mse over the workload's
     shape with MSE-only keys (its index layout and codebook size, one norm per
@@ -677,6 +686,8 @@ def bench_mse(args, w, device) -> dict:
     base = {"q": torch.from_numpy(q).to(device), "idx": torch.from_numpy(idx).to(device),
             "norm": torch.from_numpy(norm).to(device)}
     nbytes = mse_bytes(w)
+    # tq_score_mse picks its kernel form by the same rule as tq_score
+    mse_kernel = tq.tq_score_kernel_name(w.layout, bits, w.C, w.P, w.B, w.S, w.D)
     nsets = max(2, min(64, math.ceil(RING_BYTES / nbytes)))
     ring = []
     for _ in range(nsets):
@@ -739,12 +750,12 @@ def bench_mse(args, w, device) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate",
+        "dtype": score_dtype(mse_kernel),
         "data": "synthetic: seeded random MSE codes and norms, N(0,1) queries, random Hadamard signs",
         "config": {"workload": w.name, "path": "mse", "P": w.P, "H": w.H, "B": w.B, "S": w.S, "D": w.D, "C": w.C,
                    "layout": w.layout, "bits": w.bits},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "score_mfma_kernel (MSE-only)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": f"{mse_kernel} (MSE-only form)",
                      "bytes_per_launch": nbytes, "avg_launch_us": sc_us},
         "tq_score_mse_us": sc_us,
         "tq_query_transform_hadamard_us": qt_us,
@@ -1150,7 +1161,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA on hi/lo-split fp32 operands, f32 accumulate",
+        "dtype": score_dtype(kname),
         "data": "synthetic: seeded random codes, N(0,1) queries, Haar rotation, Gaussian projection",
         "config": {"workload": w.name, "P": w.P, "B": w.B, "S": w.S, "D": w.D, "C": w.C,
                    "layout": w.layout, "bits": w.bits},
