@@ -284,11 +284,14 @@ def stream_probe(device, nbytes: int) -> dict:
             "bytes": 2 * half, "us": us, "GB_s": 2 * half / (us * 1e-6) / 1e9}
 
 
-def stream_probes(device, read_bytes: int, write_bytes: int, steps: int) -> dict:
+def stream_probes(device, read_bytes: int, write_bytes: int, steps: int, tile=None) -> dict:
     """The library's streaming probes at the workload's byte counts: tq_probe_read
     over read_bytes (the key codes of one launch), tq_probe_write over
     write_bytes (its scores), and tq_probe_read_write (each workgroup reads its
     slice of the codes, then writes its slice of the scores from what it read).
+    With tile = (B, S, D) (unpacked keys, one 32-query tile) also tq_probe_tile:
+    the unpacked scorer's own loads and stores in its own grid, without its
+    arithmetic (the read buffer holds the index rows, the sign rows and gamma).
     Each is launched over a ring of distinct buffers (>= 512 MB, so no launch
     finds its bytes in the caches), captured in a graph and replayed back to
     back, timed with HIP events on the launching stream -- the same method as
@@ -316,6 +319,10 @@ def stream_probes(device, read_bytes: int, write_bytes: int, steps: int) -> dict
             rc = lib.tq_probe_read(vp(src.data_ptr()), ctypes.c_size_t(rb), vp(sink.data_ptr()), st)
         elif kind == "write":
             rc = lib.tq_probe_write(vp(dst.data_ptr()), ctypes.c_size_t(wb), st)
+        elif kind == "tile":
+            B, S, D = tile
+            ck = tq._CKeys(0, 0, src.data_ptr(), src.data_ptr() + S * D, src.data_ptr() + 2 * S * D)
+            rc = lib.tq_probe_tile(ctypes.byref(ck), vp(dst.data_ptr()), B, S, D, st)
         else:
             rc = lib.tq_probe_read_write(vp(src.data_ptr()), ctypes.c_size_t(rb), vp(dst.data_ptr()),
                                          ctypes.c_size_t(wb), st)
@@ -326,7 +333,8 @@ def stream_probes(device, read_bytes: int, write_bytes: int, steps: int) -> dict
                    "HIP events",
            "ring_pairs": npairs}
     reps = max(2, steps // npairs)
-    for kind, nbytes in (("read", rb), ("write", wb), ("read_write", rb + wb)):
+    kinds = [("read", rb), ("write", wb), ("read_write", rb + wb)] + ([("tile", rb + wb)] if tile else [])
+    for kind, nbytes in kinds:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for src, dst in pairs:
@@ -1204,14 +1212,20 @@ def main() -> int:
         }
         log(f"f16 single pass ({f16_name}): {f16_us:.2f} us per tq_score launch ({f16_gbs:.0f} GB/s)")
     if not args.no_stream_probe:
-        probes = stream_probes(device, w.key_bytes(), w.score_bytes(), args.steps)
+        tile = (w.B, w.S, w.D) if (w.layout == "unpacked" and w.P == 1 and w.B <= 32 and w.D in (64, 128, 256)) else None
+        probes = stream_probes(device, w.key_bytes(), w.score_bytes(), args.steps, tile)
         rw = probes["read_write"]
         probes["tq_score_time_over_read_write"] = score_us / rw["us"]
+        if tile:
+            probes["tq_score_time_over_tile"] = score_us / probes["tile"]["us"]
         out["stream_probes"] = probes
         log(f"probes: read {probes['read']['bytes'] / 1e6:.2f} MB in {probes['read']['us']:.2f} us, "
             f"write {probes['write']['bytes'] / 1e6:.2f} MB in {probes['write']['us']:.2f} us, "
             f"read-then-write {rw['us']:.2f} us ({rw['GB_s']:.0f} GB/s); tq_score takes "
             f"{probes['tq_score_time_over_read_write']:.2f}x the read-then-write probe")
+        if tile:
+            log(f"tile-pattern probe (the scorer's loads and stores, no arithmetic): {probes['tile']['us']:.2f} us; "
+                f"tq_score takes {probes['tq_score_time_over_tile']:.2f}x it")
         probe = stream_probe(device, alg_bytes)
         probe["tq_score_frac_of_probe"] = achieved / probe["GB_s"]
         out["stream_probe"] = probe

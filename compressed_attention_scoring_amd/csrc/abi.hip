@@ -486,4 +486,19 @@ int tq_probe_read_write(const void* src, size_t read_bytes, void* dst, size_t wr
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 
+int tq_probe_tile(const tq_keys* keys, float* out, int B, int S, int D, void* stream) {
+    if (!keys || B < 0 || S < 0 || D <= 0) return TQ_ERR_ARG;
+    if (keys->layout != TQ_UNPACKED) return TQ_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0) return TQ_OK;
+    if (!keys->idx || !keys->sign || !keys->gamma || !out) return TQ_ERR_ARG;
+    if (!tq::probe_tile_supported(B, S, D)) return TQ_ERR_UNSUPPORTED;
+    if (!aligned16(keys->idx) || !aligned16(keys->sign) || !aligned16(keys->gamma) || !aligned16(out))
+        return TQ_ERR_ALIGN;
+    const hipError_t e = tq::launch_probe_tile(static_cast<const uint8_t*>(keys->idx),
+                                               static_cast<const uint8_t*>(keys->sign),
+                                               static_cast<const float*>(keys->gamma), out, B, S, D,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
 }  // extern "C"

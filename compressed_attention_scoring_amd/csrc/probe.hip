@@ -10,7 +10,15 @@
 //  * read then write: workgroup k loads its slice of the source (two words per
 //    lane) and then stores its slice of the destination with values that
 //    depend on what it loaded, the dependency of a scoring launch (codes in,
-//    scores out) without its arithmetic.
+//    scores out) without its arithmetic;
+//  * tile pattern: the loads and stores of the unpacked 32 x 32 scorer, in its
+//    grid, without its arithmetic: each wavefront takes 32-key tiles, lane
+//    (col, g) loads half of key col's index row and half of its sign row (16
+//    bytes per lane and instruction, so an instruction touches 32 rows) and
+//    gamma, folds them into one word, and stores 16 words of the [B, S] output
+//    in the accumulator order of the matrix cores (two 128-byte rows per
+//    instruction, streaming stores through a descriptor that drops rows past B
+//    and keys past S).
 #include "tq_common.hpp"
 
 namespace tq {
@@ -62,7 +70,71 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_write_kernel(const u
     }
 }
 
+constexpr int kTileKeys = 32;
+constexpr uint32_t kWord3 = 0x00020000u;     // raw 32-bit buffer
+constexpr uint32_t kDrop = 0x80000000u;      // offset of a key past S: beyond every descriptor here
+constexpr int kStreaming = 2;                // store cache policy of the scorer
+
+template <int D>
+__global__ __launch_bounds__(kProbeThreads) void probe_tile_kernel(const uint8_t* __restrict__ idx,
+                                                                   const uint8_t* __restrict__ sign,
+                                                                   const float* __restrict__ gamma,
+                                                                   float* __restrict__ out, int B, int S) {
+    constexpr int NW = D / 2 / 16;           // 16-byte words of a lane's half row
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, g = lane >> 5;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)((uint32_t)min(B, 32) * (uint32_t)S * 4u), kWord3);
+    for (int t = blockIdx.x * 4 + wave; t < ntiles; t += gridDim.x * 4) {
+        const int key = min(t * kTileKeys + col, S - 1);
+        const uint4* pi = reinterpret_cast<const uint4*>(idx + (int64_t)key * D + g * (D / 2));
+        const uint4* ps = reinterpret_cast<const uint4*>(sign + (int64_t)key * D + g * (D / 2));
+        uint4 wi[NW], ws[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) wi[k] = pi[k];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) ws[k] = ps[k];
+        uint32_t x = __float_as_uint(gamma[key]);
+#pragma unroll
+        for (int k = 0; k < NW; ++k) x ^= wi[k].x ^ wi[k].y ^ wi[k].z ^ wi[k].w ^ ws[k].x ^ ws[k].y ^ ws[k].z ^ ws[k].w;
+        const int s = t * kTileKeys + col;
+        const uint32_t lo = s < S ? ((uint32_t)g * 4u * (uint32_t)S + (uint32_t)s) * 4u : kDrop;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            __builtin_amdgcn_raw_buffer_store_b32(x + (uint32_t)v, r,
+                                                  lo + (uint32_t)(8 * (v >> 2) + (v & 3)) * (uint32_t)S * 4u, 0,
+                                                  kStreaming);
+    }
+}
+
 }  // namespace
+
+bool probe_tile_supported(int B, int S, int D) {
+    return B >= 1 && B <= 32 && S >= 1 && S < (1 << 24) && (D == 64 || D == 128 || D == 256);
+}
+
+hipError_t launch_probe_tile(const uint8_t* idx, const uint8_t* sign, const float* gamma, float* out, int B, int S,
+                             int D, hipStream_t stream) {
+    if (!probe_tile_supported(B, S, D)) return hipErrorInvalidValue;
+    const int ntiles = (S + kTileKeys - 1) / kTileKeys;
+    // the grid of the LDS-staged scorer at one 32-query tile: a tile per
+    // wavefront up to 256 workgroups (one per compute unit), then grid-stride
+    const int grid = min((ntiles + 3) / 4, 256);
+    switch (D) {
+        case 64:
+            hipLaunchKernelGGL(probe_tile_kernel<64>, dim3(grid), dim3(kProbeThreads), 0, stream, idx, sign, gamma, out, B, S);
+            break;
+        case 128:
+            hipLaunchKernelGGL(probe_tile_kernel<128>, dim3(grid), dim3(kProbeThreads), 0, stream, idx, sign, gamma, out, B, S);
+            break;
+        default:
+            hipLaunchKernelGGL(probe_tile_kernel<256>, dim3(grid), dim3(kProbeThreads), 0, stream, idx, sign, gamma, out, B, S);
+            break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
     const int64_t n16 = bytes / 16;

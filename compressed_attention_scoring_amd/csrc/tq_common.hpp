@@ -126,6 +126,10 @@ hipError_t launch_attend_combine(const float* ws, const float* Pi_v, float* out,
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_probe_write(void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_probe_read_write(const void* src, int64_t rbytes, void* dst, int64_t wbytes, hipStream_t stream);
+// The unpacked 32 x 32 scorer's loads and stores without its arithmetic (B <= 32).
+bool probe_tile_supported(int B, int S, int D);
+hipError_t launch_probe_tile(const uint8_t* idx, const uint8_t* sign, const float* gamma, float* out, int B, int S,
+                             int D, hipStream_t stream);
 
 hipError_t launch_decode(KeyStreams keys, int layout, int bits,
                          uint8_t* idx_out, int8_t* sign_out, float* gamma_out,

@@ -477,6 +477,24 @@ int tq_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 int tq_probe_write(void* dst, size_t bytes, void* stream);
 int tq_probe_read_write(const void* src, size_t read_bytes, void* dst, size_t write_bytes, void* stream);
 
+/*
+ * tq_probe_tile: the memory traffic of tq_score's LDS-staged kernel on
+ * unpacked keys with one 32-query tile (the decode shape), without its
+ * arithmetic, in the same grid: every wavefront takes 32-key tiles; lane
+ * (k, g), k = lane % 32, g = lane / 32, loads bytes [g D/2, (g+1) D/2) of key
+ * k's index and sign rows (16 bytes per instruction) and gamma[k], folds them
+ * into x = bits(gamma) ^ (xor of those 32-bit words), and stores x + v as the
+ * bits of out[row, key] for v = 0..15, row = 8 (v / 4) + 4 g + v % 4 (rows
+ * past B and keys past S are not written).
+ *   keys  unpacked (idx uint8 [S, D], sign int8 [S, D], gamma fp32 [S])
+ *   out   float32 [B, S]
+ * B <= 32, S < 2^24, D in {64, 128, 256}. TQ_ERR_ARG for a null pointer or a
+ * negative size, TQ_ERR_UNSUPPORTED for packed keys or other shapes,
+ * TQ_ERR_ALIGN for a buffer that is not 16-byte aligned; B = 0 or S = 0 is a
+ * no-op.
+ */
+int tq_probe_tile(const tq_keys* keys, float* out, int B, int S, int D, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@ EXPECTED = {
     "tq_decode_debug", "tq_compress_keys", "tq_status_string", "tq_attend", "tq_attend_workspace_bytes",
     "tq_query_transform_hadamard", "tq_score_mse", "tq_query_transform_split", "tq_score_split",
     "tq_score_attend", "tq_score_attend_workspace_bytes", "tq_score_attend_with_mode", "tq_attend_no_alloc",
-    "tq_probe_read", "tq_probe_write", "tq_probe_read_write",
+    "tq_probe_read", "tq_probe_write", "tq_probe_read_write", "tq_probe_tile",
 }
 OK, ARG, UNSUP, ALIGN = 0, -1, -2, -3
 
@@ -290,3 +290,15 @@ def test_probe_argument_checks_host_only():
     assert lib.tq_probe_write(a8, sz(32), None) == ALIGN
     assert lib.tq_probe_read_write(a16, sz(0), a16, sz(16), None) == ARG
     assert lib.tq_probe_read_write(a16, sz(16), a8, sz(16), None) == ALIGN
+    t = lib.tq_probe_tile
+    assert t(None, a16, 32, 64, 128, None) == ARG
+    assert t(ctypes.byref(_keys()), a16, 0, 64, 128, None) == OK            # empty
+    assert t(ctypes.byref(_keys()), a16, 32, 0, 128, None) == OK
+    assert t(ctypes.byref(_keys()), None, 32, 64, 128, None) == ARG
+    assert t(ctypes.byref(_keys()), a16, -1, 64, 128, None) == ARG
+    assert t(ctypes.byref(_keys(layout=1, bits=2)), a16, 32, 64, 128, None) == UNSUP
+    assert t(ctypes.byref(_keys()), a16, 33, 64, 128, None) == UNSUP        # one 32-query tile
+    assert t(ctypes.byref(_keys()), a16, 32, 64, 96, None) == UNSUP
+    assert t(ctypes.byref(_keys()), a16, 32, 1 << 24, 128, None) == UNSUP
+    assert t(ctypes.byref(_keys(idx=17)), a16, 32, 64, 128, None) == ALIGN
+    assert t(ctypes.byref(_keys()), a8, 32, 64, 128, None) == ALIGN

@@ -51,6 +51,37 @@ def test_read_write_probe(rbytes, wbytes):
     assert bool((w == torch.tensor([0, 1, 2, 3], dtype=torch.int32)).all())
 
 
+@pytest.mark.parametrize("B,S,D", [(32, 32768, 128), (5, 1000, 128), (32, 70, 64), (1, 33, 256)])
+def test_tile_probe(B, S, D):
+    """tq_probe_tile reads every code byte of the unpacked keys and writes every
+    score slot once, in the scorer's lane order: out[row, key] holds the xor of
+    the 32-bit words of key's half rows (half (row / 4) % 2) and gamma's bits,
+    plus the accumulator element v of that row."""
+    import numpy as np
+
+    say(f"probe tile B={B} S={S} D={D}")
+    rng = np.random.default_rng(S + D)
+    idx = rng.integers(0, 256, size=(S, D), dtype=np.uint8)
+    sign = rng.integers(0, 256, size=(S, D), dtype=np.uint8)
+    gam = rng.standard_normal(S).astype(np.float32)
+    keys = tq.Keys("unpacked", torch.from_numpy(idx).cuda(), torch.from_numpy(sign.view(np.int8)).cuda(),
+                   torch.from_numpy(gam).cuda())
+    ck, _, _ = keys._c(D)
+    out = torch.full((B, S), float("nan"), dtype=torch.float32, device="cuda:0")
+    rc = tq._lib.tq_probe_tile(ctypes.byref(ck), ctypes.c_void_p(out.data_ptr()), B, S, D, _st())
+    assert rc == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    half = D // 2
+    words = lambda a, g: np.bitwise_xor.reduce(a[:, g * half:(g + 1) * half].copy().view(np.uint32), axis=1)
+    x = [words(idx, g) ^ words(sign, g) ^ gam.view(np.uint32) for g in (0, 1)]
+    rows = np.arange(B)
+    g = (rows >> 2) & 1
+    v = 4 * (rows >> 3) + (rows & 3)
+    want = np.stack([(x[g[r]] + np.uint32(v[r])).astype(np.uint32) for r in rows])
+    assert np.array_equal(got, want)
+
+
 def test_read_probe_leaves_sink():
     say("probe read")
     src = torch.zeros(8519680 // 4, dtype=torch.int32, device="cuda:0")
