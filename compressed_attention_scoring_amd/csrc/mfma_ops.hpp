@@ -94,6 +94,38 @@ __device__ __forceinline__ void store_score(__amdgpu_buffer_rsrc_t r, uint32_t o
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kNonTemporal);
 }
 
+// A raw buffer over `keys` rows of `row` bytes from `base`: loads past it
+// return zero without a memory request, so a tile past the last key (or the
+// keys past S in the last tile) costs no traffic while every load still
+// issues. `keys` must be uniform across the wavefront.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t key_rows(const void* base, int keys, int row) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, keys * row, kBufferWord3);
+}
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// N dwords at byte offset `off` (4-byte aligned) of buffer r, in the widest loads.
+template <int N>
+__device__ __forceinline__ void buffer_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[N]) {
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= N; i += 4) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4u * i, 0, 0);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+    }
+    if constexpr (N % 4 == 3) {
+        const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4u * i, 0, 0);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z;
+    } else if constexpr (N % 4 == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4u * i, 0, 0);
+        w[i] = v.x; w[i + 1] = v.y;
+    } else if constexpr (N % 4 == 1) {
+        w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4u * i, 0, 0);
+    }
+}
+
 // Codebook byte tables for lut4: the entries (up to 8, zero beyond C) times a
 // power of two sc, split into f16 hi and lo parts.
 __device__ __forceinline__ void codebook_tables(const float* __restrict__ codebook, int C, float& sc,

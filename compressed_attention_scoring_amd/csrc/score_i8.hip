@@ -103,35 +103,94 @@ __global__ __launch_bounds__(kThreads, MINW) void score_i8_kernel(
     const int ntiles = (S + kTileKeys16 - 1) / kTileKeys16;
     int tile = blockIdx.x * kWaves + wave;
     const int stride = gridDim.x * kWaves;
-    if (tile >= ntiles) return;                    // no barrier in this kernel
     const int gq = lane >> 4;                      // lane group: coordinate quarter / output query
     const int kc = lane & 15;                      // key column
     const int r = lane & 15;                       // operand row = 4 q + limb
     const int rq = r >> 2, rt = r & 3;
     const int64_t key0 = (int64_t)p * S;
 
-    // this lane's quarter of query rq's rows of A and T (queries past B are
-    // computed from the last one and never stored)
-    const int64_t qoff = ((int64_t)p * B + b0 + min(rq, nb - 1)) * D + gq * Q;
-    float xa[Q], xt[Q];
-#pragma unroll
-    for (int k = 0; k < Q; k += 4) {
-        const float4 va = *reinterpret_cast<const float4*>(A + qoff + k);
-        xa[k] = va.x; xa[k + 1] = va.y; xa[k + 2] = va.z; xa[k + 3] = va.w;
-        if constexpr (QJL) {
-            const float4 vt = *reinterpret_cast<const float4*>(T + qoff + k);
-            xt[k] = vt.x; xt[k + 1] = vt.y; xt[k + 2] = vt.z; xt[k + 3] = vt.w;
-        } else {
-            xt[k] = xt[k + 1] = xt[k + 2] = xt[k + 3] = 0.f;
-        }
-    }
-    // Code buffers: each tile's codes are requested four tiles ahead (a packed
-    // tile's codes are 3-5 registers a lane).
     constexpr int NBUF = 5;
     TileCodes<NI, NS> codes[NBUF];
-    asm volatile("" ::: "memory");
-    load_quarter<1, BITS, D, QJL>(codes[0], idx, sign, gamma, key0 + min(tile * kTileKeys16 + kc, S - 1), gq);
-    asm volatile("" ::: "memory");
+    // This lane's quarter of tile t's codes, through descriptors that cover the
+    // tile's keys: a tile past the end, and keys past S, load nothing.
+    constexpr int IQ = SF::IDX_ROW / 4, SQ = SF::SIGN_ROW / 4;
+    const uint32_t ioff = (uint32_t)(kc * SF::IDX_ROW + gq * IQ);
+    const uint32_t soff = (uint32_t)(kc * SF::SIGN_ROW + gq * SQ);
+    auto load = [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
+        const int nk = __builtin_amdgcn_readfirstlane(max(0, min(kTileKeys16, S - t * kTileKeys16)));
+        const int64_t k0 = key0 + (nk > 0 ? (int64_t)t * kTileKeys16 : 0);
+        buffer_dwords<NI>(key_rows(idx + k0 * SF::IDX_ROW, nk, SF::IDX_ROW), ioff, c.iw);
+        if constexpr (QJL) buffer_dwords<NS>(key_rows(sign + k0 * SF::SIGN_ROW, nk, SF::SIGN_ROW), soff, c.sw);
+        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(
+            key_rows(static_cast<const _Float16*>(gamma) + k0, nk, 2), (uint32_t)kc * 2u, 0, 0);
+        c.gam = (float)__builtin_bit_cast(_Float16, h);
+    };
+
+    // The query operands are the same for the four wavefronts of the workgroup,
+    // and a limb decomposition serves the four lanes that differ only in the
+    // limb they take; so the workgroup decomposes each of the 8 D values of its
+    // four rows of A and T once into a shared table, and every lane then
+    // gathers its operand bytes from it. Thread t takes VPT consecutive
+    // coordinates of row (t / 32) % 4 of A (t < 128) or T; a row's 32 threads
+    // share a half wavefront, so its maximum and its limb sums reduce over it.
+    // Rows past B re-read the last query and are never stored.
+    constexpr int VPT = D / 32;                    // values per thread
+    constexpr int QP = Q + 1;                      // table stride of a quarter row (bank spread)
+    constexpr int RS = 4 * QP + 4;                 // table stride of a row
+    __shared__ uint32_t limbs[2][4 * RS];          // [A or T][row, quarter, coordinate]: four int8 limbs
+    __shared__ float row_scale[2][4];
+    __shared__ int row_tsum[4][4];
+    {
+        const int t = threadIdx.x;
+        const int type = t >> 7, row = (t >> 5) & 3, c0 = (t & 31) * VPT;
+        const float* src = (type == 0 ? A : T) + ((int64_t)p * B + b0 + min(row, nb - 1)) * D + c0;
+        float x[VPT];
+        if (type == 0 || QJL) {
+#pragma unroll
+            for (int k = 0; k < VPT; k += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(src + k);
+                x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) x[k] = 0.f;
+        }
+        // Code buffers: each tile's codes are requested four tiles ahead (a
+        // packed tile's codes are 3-5 registers a lane); the first tile's right
+        // behind this thread's row values, so the table waits for those only.
+        asm volatile("" ::: "memory");
+        load(codes[0], tile);
+        asm volatile("" ::: "memory");
+        float m = 0.f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) m = fmaxf(m, fabsf(x[k]));
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float sx = limb_scale(m);
+        int ls[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            int l[4];
+            int8_limbs(x[k] * sx, l);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) ls[n] += l[n];
+            const int c = c0 + k;
+            limbs[type][row * RS + (c / Q) * QP + c % Q] = pack_limbs(l);
+        }
+        if (type == 1) {                           // uniform: wavefronts 2 and 3
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) ls[n] += __shfl_xor(ls[n], o);
+        }
+        if ((t & 31) == 0) {
+            row_scale[type][row] = sx;
+            if (type == 1) {
+#pragma unroll
+                for (int n = 0; n < 4; ++n) row_tsum[row][n] = ls[n];
+            }
+        }
+    }
 
     // codebook limb tables: tab[m] = limb m of entries 0-3 (dword 0) and 4-7
     float cbv[8], mc = 0.f;
@@ -150,64 +209,45 @@ __global__ __launch_bounds__(kThreads, MINW) void score_i8_kernel(
         tab[1][e >> 2] = put_byte(tab[1][e >> 2], e & 3, l[1]);
         tab[2][e >> 2] = put_byte(tab[2][e >> 2], e & 3, l[2]);
     }
-
-    // row scales: maxima over the row's four quarters (lanes r, r + 16, r + 32, r + 48)
-    float ma = 0.f, mt = 0.f;
-#pragma unroll
-    for (int k = 0; k < Q; ++k) {
-        ma = fmaxf(ma, fabsf(xa[k]));
-        mt = fmaxf(mt, fabsf(xt[k]));
-    }
-    ma = fmaxf(ma, __shfl_xor(ma, 16));
-    ma = fmaxf(ma, __shfl_xor(ma, 32));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float sA = limb_scale(ma), sT = limb_scale(mt);
+    __syncthreads();
+    if (tile >= ntiles) return;                    // after the only barrier of this kernel
 
     // Query operands. ca[m][v]: against codebook limb m in k-step v, row type t
     // holds limb t - m of A (zero when t < m). ts[v]: row type t holds limb t of
-    // T. The four limbs of a value are packed as the bytes of a dword and picked
-    // by a per-lane shift and mask, so that the selection is arithmetic. Sums of
-    // T's limbs over the whole row (for sigma = 2b - 1) are reduced over the
-    // quarters.
-    const int sh1 = 8 * max(rt - 1, 0), sh2 = 8 * max(rt - 2, 0);
-    const uint32_t mk1 = rt >= 1 ? 0xffu : 0u, mk2 = rt >= 2 ? 0xffu : 0u;
+    // T. Byte k of an operand dword is a byte of coordinate k's limb dword:
+    // two byte permutes pick it from four table words (selector byte 12 gives 0).
+    auto gather = [](const uint32_t (&d)[4], uint32_t sel_lo, uint32_t sel_hi) __attribute__((always_inline)) {
+        return perm(d[1], d[0], sel_lo) | perm(d[3], d[2], sel_hi);
+    };
+    auto sels = [](int b, uint32_t& lo, uint32_t& hi) __attribute__((always_inline)) {
+        lo = b < 0 ? 0x0C0C0C0Cu : (uint32_t)b | ((uint32_t)(4 + b) << 8) | 0x0C0C0000u;
+        hi = b < 0 ? 0x0C0C0C0Cu : 0x00000C0Cu | ((uint32_t)b << 16) | ((uint32_t)(4 + b) << 24);
+    };
+    uint32_t sl[3], sh[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) sels(rt - m, sl[m], sh[m]);
+    const uint32_t* la_row = &limbs[0][rq * RS + gq * QP];
+    const uint32_t* lt_row = &limbs[1][rq * RS + gq * QP];
     uint32_t ca[3][NV][4], ts[NV][4];
-    int tsum[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            uint32_t o0 = 0u, o1 = 0u, o2 = 0u, ot = 0u;
+            uint32_t da[4], dt[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                int la[4], lt[4];
-                int8_limbs(xa[mse_dim<1, BITS>(2 * v + w / 2, 4 * (w % 2) + k)] * sA, la);
-                int8_limbs(xt[32 * (v / 2) + 4 * (v % 2) + w + 8 * k] * sT, lt);
-#pragma unroll
-                for (int n = 0; n < 4; ++n) tsum[n] += lt[n];
-                const uint32_t pa = pack_limbs(la), pt = pack_limbs(lt);
-                o0 |= ((pa >> (8 * rt)) & 0xffu) << (8 * k);
-                o1 |= ((pa >> sh1) & mk1) << (8 * k);
-                o2 |= ((pa >> sh2) & mk2) << (8 * k);
-                ot |= ((pt >> (8 * rt)) & 0xffu) << (8 * k);
+                da[k] = la_row[mse_dim<1, BITS>(2 * v + w / 2, 4 * (w % 2) + k)];
+                if constexpr (QJL) dt[k] = lt_row[32 * (v / 2) + 4 * (v % 2) + w + 8 * k];
             }
-            ca[0][v][w] = o0;
-            ca[1][v][w] = o1;
-            ca[2][v][w] = o2;
-            ts[v][w] = ot;
-        }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        tsum[n] += __shfl_xor(tsum[n], 16);
-        tsum[n] += __shfl_xor(tsum[n], 32);
-    }
-    // epilogue factors of output query gq (row scales of lane 4 gq, whose row is
-    // query gq's): M / (sA sc) and (coef / sT) gamma (2 R_b - sum T)
-    const float kx = inv_scales(__shfl(sA, 4 * gq), sc);
-    const float ky = coef / __shfl(sT, 4 * gq);
-    const float tsum_out = weighted(__shfl(tsum[0], 4 * gq), __shfl(tsum[1], 4 * gq), __shfl(tsum[2], 4 * gq),
-                                    __shfl(tsum[3], 4 * gq));
+            for (int m = 0; m < 3; ++m) ca[m][v][w] = gather(da, sl[m], sh[m]);
+            if constexpr (QJL) ts[v][w] = gather(dt, sl[0], sh[0]);
+        }
+    // epilogue factors of output query gq: M / (sA sc) and (coef / sT) gamma (2 R_b - sum T)
+    const float kx = inv_scales(row_scale[0][gq], sc);
+    const float ky = coef / row_scale[1][gq];
+    float tsum_out = 0.f;
+    if constexpr (QJL) tsum_out = weighted(row_tsum[gq][0], row_tsum[gq][1], row_tsum[gq][2], row_tsum[gq][3]);
 
     const __amdgpu_buffer_rsrc_t out_r = score_rows(scores + ((int64_t)p * B + b0) * S, nb, S);
 
@@ -251,10 +291,6 @@ __global__ __launch_bounds__(kThreads, MINW) void score_i8_kernel(
         }
     };
 
-    auto load = [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
-        load_quarter<1, BITS, D, QJL>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys16 + kc, S - 1),
-                                      gq);
-    };
 #pragma unroll
     for (int k = 1; k < NBUF - 1; ++k) load(codes[k], tile + k * stride);
     rotate_tiles<NBUF>(codes, tile, stride, ntiles, load, tile_scores);
