@@ -512,6 +512,38 @@ __device__ __forceinline__ void load_tile(TileCodes<Fmt<LAYOUT, BITS>::template 
     else c.gam = (float)reinterpret_cast<const _Float16*>(gamma)[key];
 }
 
+// The same codes for tile t of a problem whose keys start at key0 (kTileKeys
+// keys per tile; the lane's key is t * kTileKeys + col), through descriptors
+// that cover the tile's keys below S: a tile past the end loads nothing and
+// moves no bytes, keys past S read as zero. t must be uniform across the
+// wavefront.
+template <int LAYOUT, int BITS, int D, bool QJL = true>
+__device__ __forceinline__ void load_tile_at(TileCodes<Fmt<LAYOUT, BITS>::template idx_dw<D>(),
+                                                       Fmt<LAYOUT, BITS>::template sign_dw<D>()>& c,
+                                             const uint8_t* __restrict__ idx, const uint8_t* __restrict__ sign,
+                                             const void* __restrict__ gamma, int64_t key0, int t, int S, int col,
+                                             int m) {
+    using F = Fmt<LAYOUT, BITS>;
+    constexpr int NI = F::template idx_dw<D>();
+    constexpr int NS = F::template sign_dw<D>();
+    constexpr int IDX_ROW = F::template idx_row<D>();
+    constexpr int SIGN_ROW = F::template sign_row<D>();
+    const int nk = __builtin_amdgcn_readfirstlane(max(0, min(kTileKeys, S - t * kTileKeys)));
+    const int64_t k0 = key0 + (nk > 0 ? (int64_t)t * kTileKeys : 0);
+    buffer_dwords<NI>(key_rows(idx + k0 * IDX_ROW, nk, IDX_ROW), (uint32_t)(col * IDX_ROW + m * (IDX_ROW / 2)), c.iw);
+    if constexpr (QJL)
+        buffer_dwords<NS>(key_rows(sign + k0 * SIGN_ROW, nk, SIGN_ROW), (uint32_t)(col * SIGN_ROW + m * (SIGN_ROW / 2)),
+                          c.sw);
+    if constexpr (LAYOUT == 0) {
+        c.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              key_rows(static_cast<const float*>(gamma) + k0, nk, 4), (uint32_t)col * 4u, 0, 0));
+    } else {
+        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(key_rows(static_cast<const _Float16*>(gamma) + k0, nk, 2),
+                                                                (uint32_t)col * 2u, 0, 0);
+        c.gam = (float)__builtin_bit_cast(_Float16, h);
+    }
+}
+
 // Position of operand lane p's 16-byte slot in the LDS block of k-step j. The
 // blocks of different k-steps sit 4 KiB apart (the same banks), so the eight
 // 16-coordinate blocks of a query row, written together in the prologue, would

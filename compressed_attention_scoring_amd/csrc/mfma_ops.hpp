@@ -86,8 +86,12 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit buffer, gfx9 fami
 constexpr uint32_t kDropKey = 0x80000000u;       // lane offset of a key past S
 constexpr int kNonTemporal = 2;                  // cache policy: stream past the caches
 
+// `rows` is uniform across the wavefront; readfirstlane keeps the descriptor in
+// scalar registers (a clamp the compiler evaluated on the vector unit made
+// every store a loop over the distinct descriptors of the wavefront's lanes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t score_rows(float* base, int rows, int S) {
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)((uint32_t)rows * (uint32_t)S * 4u), kBufferWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)((uint32_t)__builtin_amdgcn_readfirstlane(rows) * (uint32_t)S * 4u),
+                                             kBufferWord3);
 }
 
 __device__ __forceinline__ void store_score(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {

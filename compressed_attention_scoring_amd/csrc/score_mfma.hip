@@ -131,14 +131,12 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         // only for them while the key bytes are still in flight from HBM. An empty
         // asm with a memory clobber keeps the compiler from moving the key loads
         // above the A and T loads (it emits no instruction); the key load is
-        // unconditional too (a wave without a tile re-reads a valid key).
+        // unconditional too (a wave without a tile loads nothing through it).
         if (r0 == 0) {
             asm volatile("" ::: "memory");
-            const int s = min(min(tile, ntiles - 1) * kTileKeys + col, S - 1);
-            load_tile<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma, key0 + s, g);
+            load_tile_at<LAYOUT, BITS, D, QJL>(cur, idx, sign, gamma, key0, tile, S, col, g);
             if constexpr (NBUF == 3)
-                load_tile<LAYOUT, BITS, D, QJL>(codes[1], idx, sign, gamma,
-                                                key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+                load_tile_at<LAYOUT, BITS, D, QJL>(codes[1], idx, sign, gamma, key0, tile + stride, S, col, g);
             asm volatile("" ::: "memory");
             // codebook tables; their loads come after the vector loads above so
             // their latency is not paid first
@@ -250,8 +248,7 @@ __global__ __launch_bounds__(kThreads) void score_mfma_kernel(
         rotate_tiles<NBUF>(
             codes, tile, stride, ntiles,
             [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
-                load_tile<LAYOUT, BITS, D, QJL>(c, idx, sign, gamma,
-                                                key0 + min(min(t, ntiles - 1) * kTileKeys + col, S - 1), g);
+                load_tile_at<LAYOUT, BITS, D, QJL>(c, idx, sign, gamma, key0, t, S, col, g);
             },
             tile_scores);
     }
@@ -560,10 +557,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
     TileCodes<NI, NS> codes[2];               // code buffers of the tile loop
     TileCodes<NI, NS>& cur = codes[0];
     asm volatile("" ::: "memory");
-    {
-        const int s = min(tile * kTileKeys + col, S - 1);
-        load_tile<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0 + s, g);
-    }
+    load_tile_at<LAYOUT, BITS, D>(cur, idx, sign, gamma, key0, tile, S, col, g);
     asm volatile("" ::: "memory");
     float sc;
     uint32_t tab_hi[4], tab_lo[4];
@@ -658,7 +652,7 @@ __global__ __launch_bounds__(kThreads, MINW) void score_qs_kernel(
     rotate_tiles<2>(
         codes, tile, stride, ntiles,
         [&](TileCodes<NI, NS>& c, int t) __attribute__((always_inline)) {
-            load_tile<LAYOUT, BITS, D>(c, idx, sign, gamma, key0 + min(min(t, ntiles - 1) * kTileKeys + col, S - 1), g);
+            load_tile_at<LAYOUT, BITS, D>(c, idx, sign, gamma, key0, t, S, col, g);
         },
         tile_scores);
 }
@@ -845,9 +839,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     }
     TileCodes<NI, NS> c0, c1;
     asm volatile("" ::: "memory");
-    load_tile<LAYOUT, BITS, D, QJL>(c0, idx, sign, gamma, key0 + min(tile * kTileKeys + col, S - 1), g);
-    load_tile<LAYOUT, BITS, D, QJL>(c1, idx, sign, gamma,
-                                    key0 + min(min(tile + stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+    load_tile_at<LAYOUT, BITS, D, QJL>(c0, idx, sign, gamma, key0, tile, S, col, g);
+    load_tile_at<LAYOUT, BITS, D, QJL>(c1, idx, sign, gamma, key0, tile + stride, S, col, g);
     asm volatile("" ::: "memory");
     float sc;
     uint32_t tab_hi[4], tab_lo[4];
@@ -917,12 +910,11 @@ __global__ __launch_bounds__(kThreads, 2) void score_shared_kernel(
     // tile's MFMAs are issued, and then the next tile's codes `cn` are unpacked
     // into the other buffer (its gamma kept for the next step), so the wait for
     // those codes comes after this tile's matrix work rather than before it;
-    // one barrier ends the step. Past the last tile `cn` holds a clamped valid
-    // tile whose unpacking nobody reads.
+    // one barrier ends the step. Past the last tile `cn` holds zeros whose
+    // unpacking nobody reads.
     auto step = [&](int t, uint8_t* buf, uint8_t* other, const TileCodes<NI, NS>& cn, TileCodes<NI, NS>& cr)
         __attribute__((always_inline)) {
-        load_tile<LAYOUT, BITS, D, QJL>(cr, idx, sign, gamma,
-                                        key0 + min(min(t + 2 * stride, ntiles - 1) * kTileKeys + col, S - 1), g);
+        load_tile_at<LAYOUT, BITS, D, QJL>(cr, idx, sign, gamma, key0, t + 2 * stride, S, col, g);
         f32x16 accM, accR;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { accM[v] = 0.f; accR[v] = 0.f; }
