@@ -26,7 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["abi.hip", "query_transform.hip", "score_valu.hip", "score_mfma.hip", "score_i8.hip", "decode.hip", "compress.hip", "attend.hip", "score_split.hip", "probe.hip"]
+SOURCES = ["abi.hip", "query_transform.hip", "score_valu.hip", "score_mfma.hip", "score_lds.hip", "score_reg.hip", "score_shared.hip", "score_small.hip", "score_split_mfma.hip", "score_fused.hip", "score_i8.hip", "decode.hip", "compress.hip", "attend.hip", "score_split.hip", "probe.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
