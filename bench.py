@@ -75,6 +75,50 @@ def parse():
     return ap.parse_args()
 
 
+def source_digest(files) -> str:
+    """sha256 over the code of the listed sources with comments and blank lines
+    taken out, so that a record taken on a kernel stays valid through edits
+    of its comments but not of its code. String and character literals are
+    kept whole (a "//" inside one is not a comment)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in files:
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        out, i, n = [], 0, len(text)
+        while i < n:
+            c = text[i]
+            if c in "\"'":
+                j = i + 1
+                while j < n and text[j] != c:
+                    j += 2 if text[j] == "\\" else 1
+                out.append(text[i:j + 1])
+                i = j + 1
+            elif text.startswith("//", i):
+                j = text.find("\n", i)
+                i = n if j < 0 else j
+            elif text.startswith("/*", i):
+                j = text.find("*/", i + 2)
+                i = n if j < 0 else j + 2
+            else:
+                out.append(c)
+                i += 1
+        lines = [ln.rstrip() for ln in "".join(out).split("\n")]
+        h.update(("\n".join(ln for ln in lines if ln) + "\n").encode())
+    return h.hexdigest()
+
+
+def record_matches(rec, kname=None) -> bool:
+    """True if a committed profile record was taken on the sources as they are
+    now (and, given a kernel name, on that kernel)."""
+    try:
+        digest = source_digest(rec["source_files"])
+    except (OSError, KeyError, ValueError, UnicodeDecodeError):
+        return False
+    return digest == rec.get("source_sha256") and (kname is None or rec.get("kernel_id") == kname)
+
+
 def counters_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"tq_score_{workload}_counters.json")
 
@@ -83,18 +127,12 @@ def measured_traffic(w, kname):
     """HBM bytes per score launch from the committed counter record of this
     workload, if it was taken on the kernel that runs now with its source as it
     is now; else None."""
-    import hashlib
-
     try:
         with open(counters_path(w.name)) as f:
             rec = json.load(f)
-        h = hashlib.sha256()
-        for p in rec["source_files"]:
-            with open(os.path.join(ROOT, p), "rb") as f:
-                h.update(f.read())
-    except (OSError, KeyError, ValueError):
+    except (OSError, ValueError):
         return None
-    if h.hexdigest() != rec.get("source_sha256") or rec.get("kernel_id") != kname:
+    if not record_matches(rec, kname):
         return None
     return rec["per_dispatch"]["traffic_bytes"]
 
@@ -356,18 +394,12 @@ def trace_record(w, kname):
     """Per-dispatch durations of this workload's score kernel from the committed
     rocprofv3 kernel-trace record, if it was taken on the kernel that runs now
     with its source as it is now; else None."""
-    import hashlib
-
     try:
         with open(os.path.join(ROOT, "profiles", f"tq_score_{w.name}_kernel_trace.json")) as f:
             rec = json.load(f)
-        h = hashlib.sha256()
-        for p in rec["source_files"]:
-            with open(os.path.join(ROOT, p), "rb") as f:
-                h.update(f.read())
-    except (OSError, KeyError, ValueError):
+    except (OSError, ValueError):
         return None
-    if h.hexdigest() != rec.get("source_sha256") or rec.get("kernel_id") != kname:
+    if not record_matches(rec, kname):
         return None
     return rec
 
@@ -539,18 +571,12 @@ def attend_bytes(w) -> int:
 def attend_traffic(w):
     """HBM bytes per tq_attend call (both kernels) from the committed counter
     record of this workload, if taken with attend.hip as it is now; else None."""
-    import hashlib
-
     try:
         with open(os.path.join(ROOT, "profiles", f"tq_attend_{w.name}_counters.json")) as f:
             rec = json.load(f)
-        h = hashlib.sha256()
-        for p in rec["source_files"]:
-            with open(os.path.join(ROOT, p), "rb") as f:
-                h.update(f.read())
-    except (OSError, KeyError, ValueError):
+    except (OSError, ValueError):
         return None
-    if h.hexdigest() != rec.get("source_sha256"):
+    if not record_matches(rec):
         return None
     return rec["traffic_bytes_per_call"]
 

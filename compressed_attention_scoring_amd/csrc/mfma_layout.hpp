@@ -2,8 +2,8 @@
 // order in which each key layout's coordinates enter the contraction, the
 // key-side operand builders (codebook lookups by v_perm byte tables, signs as
 // f16 +-1), the code loads of one lane, and the LDS slots of the query-side
-// operands that the workgroup builds once. Shared by the LDS-staged kernels
-// (score_mfma.hip, score_pair.hip).
+// operands that the workgroup builds once. Shared by the 32 x 32 families
+// (score_lds.hip, score_reg.hip, score_shared.hip, score_fused.hip).
 //
 // v_mfma_f32_32x32x16_f16: lane l supplies row (or column) l % 32 and
 // contraction elements 8 (l / 32) .. 8 (l / 32) + 7 of each 16-wide k-step;

@@ -16,7 +16,7 @@
 // section "v6: Fused Vectorized Hybrid", extracts 2-bit fields the same way).
 //
 // This family is the general fallback (odd D, tiny problems); the matrix-core
-// family in score_mfma.hip is the fast path where it applies.
+// families (dispatched by score_mfma.hip) are the fast path where it applies.
 #include "tq_common.hpp"
 
 namespace tq {

@@ -111,7 +111,7 @@ hipError_t launch_score_split(const float* A_hi, const float* A_lo, SplitStreams
                               int B, int S, int D_hi, int D_lo, hipStream_t stream);
 
 // Fused decode step: scores, online softmax and values in one pass
-// (score_mfma.hip), writing the attend workspace records; then the attend
+// (score_fused.hip), writing the attend workspace records; then the attend
 // combine (attend.hip).
 void score_attend_plan(int P, int B, int S, int& chunk, int& nch);
 bool score_attend_supported(int layout, int bits, int C, int vlayout, int vbits, int VC, int D);
