@@ -3,6 +3,8 @@ committed profile records to the code they were taken on."""
 import glob
 import json
 import os
+import subprocess
+import sys
 
 import bench
 
@@ -50,3 +52,12 @@ def test_records_name_existing_sources():
         for s in rec["source_files"]:
             assert os.path.isfile(os.path.join(ROOT, s)), (p, s)
         assert len(rec["source_sha256"]) == 64, p
+
+
+def test_more_than_one_gpu_is_refused():
+    """--gpus N with N > 1 prints why and exits before touching a GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["n_gpus"] == 2 and "one GPU" in d["error"]
